@@ -1,0 +1,7 @@
+"""fp64 CPU oracle of the fused chunked top-K KL loss -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path never does.
+"""
+from . import kl_oracle  # noqa: F401
+from .kl_oracle import *  # noqa: F401,F403
