@@ -1,0 +1,160 @@
+/*
+ * kdtopk.h -- C ABI of the fused chunked top-K KL distillation loss on AMD
+ * MI355X (gfx950).
+ *
+ * The operation is the loss described in "Distilling an LLM on One GPU:
+ * Offline Top-K Logits and a Fused Chunked KL Loss" (developersdigest.tech,
+ * section "The two changes") and in the scitechpulse.com news item: the student
+ * hidden states H[N,D] are projected through the LM head W[V,D] one chunk of
+ * positions at a time, each chunk's logits are folded into a running KL loss
+ * against an offline teacher cache (top-K token ids and logits per position)
+ * and discarded, and the backward pass recomputes each chunk's logits instead
+ * of storing them.  No [N,V] logits grid is ever written to device memory.
+ *
+ * Definitions (fp32 arithmetic on bf16 inputs, fp32 accumulation):
+ *   z[n,v]   = (H[n,:] . W[v,:]) / T                       student logits
+ *   lse[n]   = log sum_v exp(z[n,v])                        full vocabulary
+ *   p[n,k]   = softmax_k(topk_logit[n,:] / T)               teacher, renormalised over K
+ *   KL_n     = sum_k p[n,k] (log p[n,k] - z[n,idx[n,k]] + lse[n])   (0 log 0 = 0)
+ *   loss     = (1/N) sum_n KL_n
+ *   G[n,v]   = g/(N T) (exp(z[n,v] - lse[n]) - sum_{k: idx[n,k]=v} p[n,k]),  g = *grad_loss or 1
+ *   dH       = G W          (overwritten, bf16)
+ *   dW      += G^T H        (accumulated, fp32)
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are dense row-major.  bf16 tensors are passed as uint16_t
+ *     bit patterns.  Every data pointer is a DEVICE pointer owned by the
+ *     caller; the library never allocates, frees or retains device memory.
+ *   - H, W, dH and dW must be 16-byte aligned; idx, topk_logit, lse, row_kl
+ *     and loss 4-byte aligned.  D must be a multiple of 8.
+ *   - Limits: 1 <= K <= min(V, KD_MAX_K); 1 <= V <= KD_MAX_V; N >= 0;
+ *     chunk >= 1 (a chunk larger than N is clamped to N; the last chunk may be
+ *     ragged); T finite and > 0.
+ *   - Calls only enqueue work on hip_stream (a hipStream_t, NULL = the null
+ *     stream) and return; nothing synchronises the host.  Outputs are valid
+ *     when the stream reaches the end of the call.  Asynchronous device
+ *     faults surface at the caller's next synchronisation.
+ *   - Arguments are checked on the host before any HIP call; an invalid
+ *     argument returns a status and enqueues nothing.  KD_ERR_HIP reports a
+ *     failed launch; outputs are then unspecified.
+ *   - Token ids outside [0, V) give unspecified (but memory-safe) results;
+ *     kd_topk_kl_validate detects them.  Duplicate ids within a row act as
+ *     one entry holding the summed probability.
+ *   - Calls on different streams need distinct workspaces; forward and
+ *     backward may share one workspace when issued in order on one stream.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (rows with duplicate ids excepted).
+ */
+#ifndef KDTOPK_H
+#define KDTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KD_MAX_K 256
+#define KD_MAX_V (1 << 20)
+
+typedef enum kd_status {
+  KD_OK = 0,
+  KD_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad T */
+  KD_ERR_UNSUPPORTED = 2, /* valid but outside this library's limits */
+  KD_ERR_WORKSPACE = 3,   /* workspace smaller than kd_topk_kl_workspace_size */
+  KD_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} kd_status;
+
+/*
+ * Bytes of device workspace that kd_topk_kl_forward and kd_topk_kl_backward
+ * need for this problem (one size serves both).  Depends only on the
+ * arguments, never on the device.  Returns 0 for arguments that the entry
+ * points would reject.  The workspace holds one chunk's teacher
+ * probabilities and id buckets, the forward's per-vocab-tile softmax
+ * partials, one chunk's bf16 gradient G_c[chunk, V] and dH split partials:
+ * O(chunk * (V + K + D)) bytes plus 4 N bytes -- never O(N * V).
+ */
+size_t kd_topk_kl_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K,
+                                 int64_t chunk);
+
+/*
+ * Forward pass (blog section "The two changes": "processes one chunk of the
+ * sequence end to end ... folds the result into the running loss, and
+ * discards the chunk").
+ *
+ *   H          bf16 [N, D]   student hidden states (read)
+ *   W          bf16 [V, D]   LM-head weight, nn.Linear layout (read)
+ *   topk_idx   int32 [N, K]  cached teacher token ids (read)
+ *   topk_logit fp32 [N, K]   cached teacher logits, any per-row offset (read)
+ *   T          temperature applied to student and teacher
+ *   chunk      positions per chunk
+ *   loss       fp32 [1]      written: mean_n KL_n (0 when N == 0)
+ *   lse        fp32 [N]      written: student log-normaliser, needed by backward
+ *   row_kl     fp32 [N]      written when not NULL: KL_n per position
+ *   workspace  device scratch of workspace_bytes >= kd_topk_kl_workspace_size
+ */
+kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W,
+                             const int32_t* topk_idx, const float* topk_logit,
+                             int64_t N, int64_t D, int64_t V, int32_t K, float T,
+                             int64_t chunk, float* loss, float* lse, float* row_kl,
+                             void* workspace, size_t workspace_bytes,
+                             void* hip_stream);
+
+/*
+ * Backward pass (blog section "The two changes": "The backward pass
+ * recomputes each chunk on the fly"; the projection therefore runs twice).
+ *
+ *   H, W, topk_idx, topk_logit, N, D, V, K, T, chunk   as in the forward
+ *   lse        fp32 [N]  from the forward on the same inputs (read)
+ *   grad_loss  fp32 [1]  device scalar dLoss_out/dloss, or NULL for 1
+ *   dH         bf16 [N, D]  overwritten with G W
+ *   dW         fp32 [V, D]  accumulated: dW += G^T H (zero it for a fresh gradient)
+ *   workspace  as in the forward
+ */
+kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W,
+                              const int32_t* topk_idx, const float* topk_logit,
+                              const float* lse, const float* grad_loss,
+                              int64_t N, int64_t D, int64_t V, int32_t K, float T,
+                              int64_t chunk, uint16_t* dH, float* dW,
+                              void* workspace, size_t workspace_bytes,
+                              void* hip_stream);
+
+/*
+ * Debug aid, not on the hot path: checks the teacher cache's ids.
+ * d_flags (device int32 [1]) is overwritten with bit 0 set if some id lies
+ * outside [0, V) and bit 1 set if some row holds an id twice.
+ */
+kd_status kd_topk_kl_validate(const int32_t* topk_idx, int64_t N, int32_t K,
+                              int64_t V, int32_t* d_flags, void* hip_stream);
+
+/* Static, human-readable name of a status code. */
+const char* kd_status_string(kd_status s);
+
+/*
+ * Measurement aids.  kd_profile_enable(mask) makes every later launch of each
+ * kernel class i with bit i set in mask (classes KD_KERNEL_*) bracketed by
+ * HIP events recorded on the stream it is launched on; mask 0 turns this off.
+ * kd_profile_read waits for the recorded events of one class, returns their
+ * summed milliseconds and the number of launches since the last read, and
+ * clears them.
+ */
+enum {
+  KD_KERNEL_PREP = 0,
+  KD_KERNEL_LOGITS_FWD = 1,
+  KD_KERNEL_COMBINE = 2,
+  KD_KERNEL_FINALIZE = 3,
+  KD_KERNEL_LOGITS_BWD = 4,
+  KD_KERNEL_DH = 5,
+  KD_KERNEL_DH_REDUCE = 6,
+  KD_KERNEL_DW = 7,
+  KD_KERNEL_COUNT = 8
+};
+kd_status kd_profile_enable(uint32_t kernel_mask);
+kd_status kd_profile_read(int32_t kernel_id, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDTOPK_H */

@@ -1,0 +1,219 @@
+"""Fused chunked top-K KL distillation loss on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libkdtopk.so`` (declared in ``include/kdtopk.h``).
+Every step of the loss runs in the library's HIP kernels; this module only
+marshals arguments.  PyTorch provides device memory and the current stream.
+
+There is no fallback: if the library is missing, importing the entry points
+raises, so nothing can silently run elsewhere.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "lib_path", "load_library", "workspace_size", "forward", "backward", "validate",
+    "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libkdtopk.so"
+_lib = None
+
+KERNELS = {
+    "prep": 0, "logits_fwd": 1, "combine": 2, "finalize": 3,
+    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7,
+}
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem size",
+           3: "workspace too small", 4: "HIP launch failed"}
+
+
+class KDError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, 'unknown')} (status {status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Loads libkdtopk.so (built by ``python -m lm_head_top_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m lm_head_top_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(path)
+    c_i64, c_i32, c_f, c_vp, c_sz = (ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                                     ctypes.c_void_p, ctypes.c_size_t)
+    lib.kd_topk_kl_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i64]
+    lib.kd_topk_kl_workspace_size.restype = c_sz
+    lib.kd_topk_kl_forward.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_f,
+                                       c_i64, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+    lib.kd_topk_kl_forward.restype = ctypes.c_int
+    lib.kd_topk_kl_backward.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
+                                        c_i32, c_f, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]
+    lib.kd_topk_kl_backward.restype = ctypes.c_int
+    lib.kd_topk_kl_validate.argtypes = [c_vp, c_i64, c_i32, c_i64, c_vp, c_vp]
+    lib.kd_topk_kl_validate.restype = ctypes.c_int
+    lib.kd_status_string.argtypes = [ctypes.c_int]
+    lib.kd_status_string.restype = ctypes.c_char_p
+    lib.kd_profile_enable.argtypes = [ctypes.c_uint32]
+    lib.kd_profile_enable.restype = ctypes.c_int
+    lib.kd_profile_read.argtypes = [c_i32, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64)]
+    lib.kd_profile_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise KDError(status, what)
+
+
+def workspace_size(N: int, D: int, V: int, K: int, chunk: int) -> int:
+    return int(load_library().kd_topk_kl_workspace_size(N, D, V, K, chunk))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(torch, device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _check_inputs(torch, H, W, idx, t):
+    if not (H.is_cuda and W.is_cuda and idx.is_cuda and t.is_cuda):
+        raise ValueError("H, W, topk_idx and topk_logit must be device tensors")
+    if H.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise TypeError("H and W must be bfloat16")
+    if idx.dtype != torch.int32 or t.dtype != torch.float32:
+        raise TypeError("topk_idx must be int32 and topk_logit float32")
+    for name, x in (("H", H), ("W", W), ("topk_idx", idx), ("topk_logit", t)):
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    N, D = H.shape
+    V, D2 = W.shape
+    if D2 != D or idx.shape != t.shape or idx.shape[0] != N:
+        raise ValueError("shape mismatch: H[N,D], W[V,D], topk_idx/topk_logit[N,K]")
+    return N, D, V, idx.shape[1]
+
+
+def _workspace(torch, N, D, V, K, chunk, device, workspace):
+    need = workspace_size(N, D, V, K, chunk)
+    if need == 0:
+        raise KDError(1, "workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def forward(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024,
+            want_row_kl: bool = False, workspace=None):
+    """Loss (device fp32 [1]), lse (fp32 [N]) and optionally row_kl (fp32 [N])."""
+    torch = _torch()
+    N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
+    dev = H.device
+    ws = _workspace(torch, N, D, V, K, chunk, dev, workspace)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(N, dtype=torch.float32, device=dev) if want_row_kl else None
+    st = load_library().kd_topk_kl_forward(
+        _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), N, D, V, K, float(T), int(chunk),
+        _ptr(loss), _ptr(lse), _ptr(row_kl), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_forward")
+    return (loss, lse, row_kl) if want_row_kl else (loss, lse)
+
+
+def backward(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0,
+             chunk: int = 1024, dW=None, workspace=None):
+    """dH (bf16 [N, D], overwritten) and dW (fp32 [V, D], accumulated; zeros if None)."""
+    torch = _torch()
+    N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
+    dev = H.device
+    if lse.dtype != torch.float32 or lse.numel() != N or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [N]")
+    if grad_loss is not None and (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1):
+        raise ValueError("grad_loss must be a float32 device scalar")
+    ws = _workspace(torch, N, D, V, K, chunk, dev, workspace)
+    dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    if dW is None:
+        dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
+    elif dW.dtype != torch.float32 or tuple(dW.shape) != (V, D) or not dW.is_contiguous():
+        raise ValueError("dW must be a contiguous float32 [V, D] tensor")
+    gl = grad_loss.contiguous() if grad_loss is not None else None
+    st = load_library().kd_topk_kl_backward(
+        _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), _ptr(lse), _ptr(gl), N, D, V, K,
+        float(T), int(chunk), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_backward")
+    return dH, dW
+
+
+def validate(topk_idx, V: int) -> int:
+    """Bit 0: an id outside [0, V); bit 1: a repeated id within a row."""
+    torch = _torch()
+    N, K = topk_idx.shape
+    flags = torch.empty(1, dtype=torch.int32, device=topk_idx.device)
+    st = load_library().kd_topk_kl_validate(_ptr(topk_idx), N, K, V, _ptr(flags),
+                                            _stream_ptr(torch, topk_idx.device))
+    _check(st, "kd_topk_kl_validate")
+    return int(flags.item())
+
+
+def profile_enable(kernels=None):
+    """Times every launch of the named kernel classes with HIP events (None: off)."""
+    mask = 0
+    for k in ([kernels] if isinstance(kernels, str) else (kernels or [])):
+        mask |= 1 << KERNELS[k]
+    _check(load_library().kd_profile_enable(mask), "kd_profile_enable")
+
+
+def profile_read(kernel: str):
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(load_library().kd_profile_read(KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n)),
+           "kd_profile_read")
+    return ms.value, n.value
+
+
+class KDTopKKL:
+    """autograd.Function wrapper: loss = KDTopKKL.apply(H, W, topk_idx, topk_logit, T, chunk)."""
+
+    _fn = None
+
+    @classmethod
+    def apply(cls, H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024):
+        if cls._fn is None:
+            torch = _torch()
+
+            class _F(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, H, W, idx, t, T, chunk):
+                    loss, lse = forward(H, W, idx, t, T, chunk)
+                    ctx.save_for_backward(H, W, idx, t, lse)
+                    ctx.T, ctx.chunk = T, chunk
+                    return loss[0]
+
+                @staticmethod
+                def backward(ctx, g):
+                    H, W, idx, t, lse = ctx.saved_tensors
+                    gl = g.reshape(1).to(torch.float32).contiguous()
+                    dH, dW = backward(H, W, idx, t, lse, gl, ctx.T, ctx.chunk)
+                    return dH, dW.to(W.dtype), None, None, None, None
+
+            cls._fn = _F
+        return cls._fn.apply(H, W, topk_idx, topk_logit, T, chunk)

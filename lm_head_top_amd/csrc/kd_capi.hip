@@ -1,0 +1,241 @@
+// C ABI of the fused chunked top-K KL loss: argument checks, the chunk loop
+// and kernel launches on the caller's stream.  Declared in include/kdtopk.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "kd_kernels.h"
+#include "kd_plan.h"
+#include "kdtopk.h"
+
+namespace {
+
+// ---- optional per-kernel event timing (measurement aid) ----
+std::mutex g_prof_mu;
+uint32_t g_prof_mask = 0;
+struct EventPair {
+  hipEvent_t a, b;
+};
+std::vector<EventPair> g_prof_events[KD_KERNEL_COUNT];
+
+template <class F>
+hipError_t timed(int id, hipStream_t s, F&& launch) {
+  uint32_t mask;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    mask = g_prof_mask;
+  }
+  if (!(mask & (1u << id))) return launch();
+  EventPair ev{};
+  if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess) return hipErrorUnknown;
+  if (hipEventRecord(ev.a, s) != hipSuccess) return hipErrorUnknown;
+  const hipError_t e = launch();
+  if (hipEventRecord(ev.b, s) != hipSuccess) return hipErrorUnknown;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_events[id].push_back(ev);
+  return e;
+}
+
+#define KD_LAUNCH(id, stream, call)                              \
+  do {                                                           \
+    if (timed((id), (stream), [&] { return (call); }) != hipSuccess) \
+      return KD_ERR_HIP;                                         \
+  } while (0)
+
+bool bad_ptr(const void* p, size_t align) { return p == nullptr || !kd::aligned(p, align); }
+
+}  // namespace
+
+extern "C" {
+
+const char* kd_status_string(kd_status s) {
+  switch (s) {
+    case KD_OK:
+      return "ok";
+    case KD_ERR_INVALID_ARG:
+      return "invalid argument";
+    case KD_ERR_UNSUPPORTED:
+      return "unsupported problem size";
+    case KD_ERR_WORKSPACE:
+      return "workspace too small";
+    case KD_ERR_HIP:
+      return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t kd_topk_kl_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int64_t chunk) {
+  kd::Plan p;
+  if (kd::make_plan(N, D, V, K, 1.f, chunk, &p) != KD_OK) return 0;
+  return p.bytes;
+}
+
+kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                             const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                             float T, int64_t chunk, float* loss, float* lse, float* row_kl,
+                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+  kd::Plan p;
+  const kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
+  if (st != KD_OK) return st;
+  if (bad_ptr(loss, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(topk_idx, 4) ||
+                bad_ptr(topk_logit, 4) || bad_ptr(lse, 4)))
+    return KD_ERR_INVALID_ARG;
+  if (row_kl != nullptr && !kd::aligned(row_kl, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return KD_ERR_WORKSPACE;
+  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (N == 0) {
+    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
+    return KD_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* pw = reinterpret_cast<float*>(ws + p.off_p);
+  float* hw = reinterpret_cast<float*>(ws + p.off_h);
+  int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
+  uint32_t* ent = reinterpret_cast<uint32_t*>(ws + p.off_ent);
+  float* pm = reinterpret_cast<float*>(ws + p.off_pm);
+  float* ps = reinterpret_cast<float*>(ws + p.off_ps);
+  float* zsel = reinterpret_cast<float*>(ws + p.off_zsel);
+  float* rowkl = row_kl != nullptr ? row_kl : reinterpret_cast<float*>(ws + p.off_rowkl);
+  const float invT = 1.f / T;
+
+  for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
+    const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
+    const int npt = (rows + kd::kTile - 1) / kd::kTile;
+    kd::PrepArgs pa{topk_idx + row0 * K, topk_logit + row0 * K, rows, K, int(V), int(p.nvt), invT,
+                    pw, hw, boff, ent};
+    KD_LAUNCH(KD_KERNEL_PREP, s, kd::launch_prep(pa, npt, s));
+    kd::LogitsArgs la{};
+    la.W = W;
+    la.Hc = H + row0 * D;
+    la.rows = rows;
+    la.D = int(D);
+    la.V = int(V);
+    la.K = K;
+    la.nvt = int(p.nvt);
+    la.npt = npt;
+    la.c_pad = p.c_pad;
+    la.Vp = p.Vp;
+    la.invT = invT;
+    la.boff = boff;
+    la.ent = ent;
+    la.pm = pm;
+    la.ps = ps;
+    la.zsel = zsel;
+    KD_LAUNCH(KD_KERNEL_LOGITS_FWD, s, kd::launch_logits_fwd(la, s));
+    kd::CombineArgs ca{pm, ps, zsel, pw, hw, rows, K, int(p.nvt), p.c_pad, lse + row0, rowkl + row0};
+    KD_LAUNCH(KD_KERNEL_COMBINE, s, kd::launch_combine(ca, s));
+  }
+  KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, N, loss, s));
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                              const float* topk_logit, const float* lse, const float* grad_loss,
+                              int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                              uint16_t* dH, float* dW, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+  kd::Plan p;
+  const kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
+  if (st != KD_OK) return st;
+  if (bad_ptr(dW, 16)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(topk_idx, 4) ||
+                bad_ptr(topk_logit, 4) || bad_ptr(lse, 4) || bad_ptr(dH, 16)))
+    return KD_ERR_INVALID_ARG;
+  if (grad_loss != nullptr && !kd::aligned(grad_loss, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return KD_ERR_WORKSPACE;
+  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
+  if (N == 0) return KD_OK;  // nothing to accumulate
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  float* pw = reinterpret_cast<float*>(ws + p.off_p);
+  float* hw = reinterpret_cast<float*>(ws + p.off_h);
+  int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
+  uint32_t* ent = reinterpret_cast<uint32_t*>(ws + p.off_ent);
+  uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
+  float* dhp = reinterpret_cast<float*>(ws + p.off_dhp);
+  const float invT = 1.f / T;
+  const float g_scale = float(1.0 / (double(N) * double(T)));
+  const int ktiles = int(p.Vp / 64);
+  const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
+
+  for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
+    const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
+    const int npt = (rows + kd::kTile - 1) / kd::kTile;
+    kd::PrepArgs pa{topk_idx + row0 * K, topk_logit + row0 * K, rows, K, int(V), int(p.nvt), invT,
+                    pw, hw, boff, ent};
+    KD_LAUNCH(KD_KERNEL_PREP, s, kd::launch_prep(pa, npt, s));
+    kd::LogitsArgs la{};
+    la.W = W;
+    la.Hc = H + row0 * D;
+    la.rows = rows;
+    la.D = int(D);
+    la.V = int(V);
+    la.K = K;
+    la.nvt = int(p.nvt);
+    la.npt = npt;
+    la.c_pad = p.c_pad;
+    la.Vp = p.Vp;
+    la.invT = invT;
+    la.boff = boff;
+    la.ent = ent;
+    la.lse = lse + row0;
+    la.p = pw;
+    la.grad_loss = grad_loss;
+    la.g_scale = g_scale;
+    la.G = G;
+    KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
+    kd::DhArgs da{G, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
+    KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
+    if (p.dh_split > 1)
+      KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
+                kd::launch_dh_reduce(dhp, p.dh_split, rows, int(D), p.c_pad, dH + row0 * D, s));
+    kd::DwArgs wa{G, H + row0 * D, rows, int(D), int(V), p.Vp, dW};
+    KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
+  }
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_validate(const int32_t* topk_idx, int64_t N, int32_t K, int64_t V,
+                              int32_t* d_flags, void* hip_stream) {
+  if (d_flags == nullptr || !kd::aligned(d_flags, 4)) return KD_ERR_INVALID_ARG;
+  if (N < 0 || K <= 0 || V <= 0 || K > KD_MAX_K) return KD_ERR_INVALID_ARG;
+  if (N > 0 && bad_ptr(topk_idx, 4)) return KD_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (kd::launch_validate(topk_idx, N, K, V, d_flags, s) != hipSuccess) return KD_ERR_HIP;
+  return KD_OK;
+}
+
+kd_status kd_profile_enable(uint32_t kernel_mask) {
+  if (kernel_mask >> KD_KERNEL_COUNT) return KD_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_mask = kernel_mask;
+  return KD_OK;
+}
+
+kd_status kd_profile_read(int32_t kernel_id, double* total_ms, int64_t* launches) {
+  if (kernel_id < 0 || kernel_id >= KD_KERNEL_COUNT || total_ms == nullptr || launches == nullptr)
+    return KD_ERR_INVALID_ARG;
+  std::vector<EventPair> evs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    evs.swap(g_prof_events[kernel_id]);
+  }
+  double tot = 0.0;
+  kd_status st = KD_OK;
+  for (auto& e : evs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(e.b) != hipSuccess || hipEventElapsedTime(&ms, e.a, e.b) != hipSuccess)
+      st = KD_ERR_HIP;
+    tot += ms;
+    (void)hipEventDestroy(e.a);
+    (void)hipEventDestroy(e.b);
+  }
+  *total_ms = tot;
+  *launches = int64_t(evs.size());
+  return st;
+}
+
+}  // extern "C"

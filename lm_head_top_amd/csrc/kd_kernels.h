@@ -1,0 +1,92 @@
+// Launchers of the gfx950 kernels of the fused chunked top-K KL loss.
+// Each launcher enqueues one kernel on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kd_plan.h"
+
+namespace kd {
+
+// Per-chunk teacher side: p = softmax_K(t/T), h = sum p log p, and the chunk's
+// cache entries bucketed by (position tile, vocab tile).
+struct PrepArgs {
+  const int32_t* idx;   // [rows, K], already offset to the chunk's first row
+  const float* t;       // [rows, K]
+  int rows, K, V, nvt;
+  float invT;
+  float* p;             // [c_pad, K]
+  float* h;             // [c_pad]
+  int32_t* boff;        // [npt, nvt + 1]
+  uint32_t* ent;        // [npt, kTile * K]
+};
+
+// The chunk's logits tile kernel: z^T = W H_c^T / T over one (vocab tile,
+// position tile), with the forward or the backward epilogue.
+struct LogitsArgs {
+  const uint16_t* W;    // [V, D]
+  const uint16_t* Hc;   // [rows, D], offset to the chunk
+  int rows, D, V, K, nvt, npt;
+  int64_t c_pad, Vp;
+  float invT;
+  const int32_t* boff;
+  const uint32_t* ent;
+  // forward outputs
+  float* pm;            // [nvt, c_pad] tile max of z
+  float* ps;            // [nvt, c_pad] tile sum exp(z - max)
+  float* zsel;          // [c_pad, K]   z at the cached ids
+  // backward inputs / outputs
+  const float* lse;     // [rows] offset to the chunk
+  const float* p;       // [c_pad, K]
+  const float* grad_loss;  // device scalar or null
+  float g_scale;        // 1 / (N T)
+  uint16_t* G;          // [c_pad, Vp] bf16
+};
+
+struct CombineArgs {
+  const float* pm;
+  const float* ps;
+  const float* zsel;
+  const float* p;
+  const float* h;
+  int rows, K, nvt;
+  int64_t c_pad;
+  float* lse;      // [rows], offset to the chunk
+  float* rowkl;    // [rows], offset to the chunk
+};
+
+struct DhArgs {
+  const uint16_t* G;   // [c_pad, Vp]
+  const uint16_t* W;   // [V, D]
+  int rows, D, V;
+  int64_t Vp;
+  int split;           // number of K splits
+  int ktiles_per_split;
+  float* part;         // [split, c_pad, D] (split > 1)
+  uint16_t* dH;        // [rows, D] offset to the chunk (split == 1)
+  int64_t c_pad;
+};
+
+struct DwArgs {
+  const uint16_t* G;   // [c_pad, Vp]
+  const uint16_t* Hc;  // [rows, D] offset to the chunk
+  int rows, D, V;
+  int64_t Vp;
+  float* dW;           // [V, D]
+};
+
+hipError_t launch_prep(const PrepArgs& a, int npt, hipStream_t s);
+hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s);
+hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_finalize(const float* rowkl, int64_t N, float* loss, hipStream_t s);
+hipError_t launch_dh(const DhArgs& a, hipStream_t s);
+hipError_t launch_dh_reduce(const float* part, int split, int rows, int D, int64_t c_pad,
+                            uint16_t* dH, hipStream_t s);
+hipError_t launch_dw(const DwArgs& a, hipStream_t s);
+hipError_t launch_validate(const int32_t* idx, int64_t N, int K, int64_t V, int32_t* flags,
+                           hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+}  // namespace kd

@@ -1,0 +1,89 @@
+// Argument checks and workspace layout (host only, no HIP calls).
+#include "kd_plan.h"
+
+#include <cmath>
+
+namespace kd {
+
+namespace {
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int dh_split_for(int64_t c, int64_t D) {
+  // Output tiles of dH_c [c, D]; choose the smallest split that fills the
+  // reference CU count to >= 90% per round, else the best-filling one.
+  const int64_t tiles = ceil_div(c, kTile) * ceil_div(D, kTile);
+  int best = 1;
+  double best_eff = -1.0;
+  for (int s = 1; s <= kMaxDhSplit; ++s) {
+    const int64_t wg = tiles * s;
+    const int64_t rounds = ceil_div(wg, kRefCUs);
+    const double eff = double(wg) / double(rounds * kRefCUs);
+    if (wg >= kRefCUs && eff >= 0.9) return s;
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  return best;
+}
+
+kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                    Plan* plan) {
+  if (plan == nullptr) return KD_ERR_INVALID_ARG;
+  if (N < 0 || D <= 0 || V <= 0 || K <= 0 || chunk <= 0) return KD_ERR_INVALID_ARG;
+  if (!std::isfinite(T) || !(T > 0.f)) return KD_ERR_INVALID_ARG;
+  if (K > V) return KD_ERR_INVALID_ARG;
+  if (D % 8 != 0) return KD_ERR_INVALID_ARG;
+  if (K > KD_MAX_K || V > KD_MAX_V) return KD_ERR_UNSUPPORTED;
+  if (N > (int64_t(1) << 31) - 1 || D > (int64_t(1) << 20)) return KD_ERR_UNSUPPORTED;
+  if (N * int64_t(K) > (int64_t(1) << 31) - 1) return KD_ERR_UNSUPPORTED;
+
+  Plan p;
+  p.N = N;
+  p.D = D;
+  p.V = V;
+  p.K = K;
+  p.T = T;
+  const int64_t c = N > 0 ? (chunk < N ? chunk : N) : (chunk < kTile ? chunk : kTile);
+  p.chunk = c;
+  p.c_pad = ceil_div(c, kTile) * kTile;
+  p.nvt = ceil_div(V, kTile);
+  p.Vp = p.nvt * kTile;
+  p.npt = p.c_pad / kTile;
+  p.dh_split = dh_split_for(c, D);
+  if (p.c_pad * p.Vp > (int64_t(1) << 31) - 1) return KD_ERR_UNSUPPORTED;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  // teacher probabilities, per-row sum p log p, bucket offsets and entries
+  p.off_p = take(size_t(p.c_pad) * K * 4);
+  p.off_h = take(size_t(p.c_pad) * 4);
+  p.off_boff = take(size_t(p.npt) * size_t(p.nvt + 1) * 4);
+  p.off_ent = take(size_t(p.npt) * kTile * K * 4);
+  const size_t shared_end = off;
+  // forward-only region
+  p.off_pm = take(size_t(p.nvt) * p.c_pad * 4);
+  p.off_ps = take(size_t(p.nvt) * p.c_pad * 4);
+  p.off_zsel = take(size_t(p.c_pad) * K * 4);
+  p.off_rowkl = take(size_t(N > 0 ? N : 1) * 4);
+  const size_t fwd_end = off;
+  // backward-only region aliases the forward-only one
+  off = shared_end;
+  p.off_g = take(size_t(p.c_pad) * p.Vp * 2);
+  p.off_dhp = take(p.dh_split > 1 ? size_t(p.dh_split) * p.c_pad * D * 4 : 0);
+  const size_t bwd_end = off;
+  p.bytes = fwd_end > bwd_end ? fwd_end : bwd_end;
+  *plan = p;
+  return KD_OK;
+}
+
+}  // namespace kd

@@ -1,0 +1,46 @@
+// Host-side problem plan: argument checks, tiling constants and the
+// workspace layout of the fused chunked top-K KL loss.  Pure C++ (no HIP), so
+// the checks can be exercised on a machine without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kdtopk.h"
+
+namespace kd {
+
+// Tile sizes shared by the plan and the kernels.
+constexpr int kTile = 256;          // vocab rows / positions / D columns per GEMM tile
+constexpr int kMaxVocabTiles = KD_MAX_V / kTile;
+constexpr int kMaxDhSplit = 8;      // split-K factor ceiling for dH = G W
+constexpr int kRefCUs = 256;        // CU count the dH split is sized for (fixed, so plans are device independent)
+
+struct Plan {
+  int64_t N = 0, D = 0, V = 0, chunk = 0;
+  int32_t K = 0;
+  float T = 1.f;
+  int64_t c_pad = 0;   // chunk rounded up to kTile
+  int64_t nvt = 0;     // vocab tiles
+  int64_t Vp = 0;      // V rounded up to kTile (row stride of G_c)
+  int64_t npt = 0;     // position tiles per chunk
+  int dh_split = 1;    // split-K factor of the dH GEMM
+  // workspace byte offsets
+  size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0;  // shared by fwd and bwd
+  size_t off_pm = 0, off_ps = 0, off_zsel = 0, off_rowkl = 0;  // forward only
+  size_t off_g = 0, off_dhp = 0;                               // backward only (aliases forward)
+  size_t bytes = 0;
+};
+
+// Fills `plan` from the problem sizes.  Returns KD_OK or the reason the sizes
+// are rejected.  Does not look at pointers.
+kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                    Plan* plan);
+
+// Split-K factor of dH = G_c W for a chunk of `c` rows and hidden size D.
+int dh_split_for(int64_t c, int64_t D);
+
+// Pointer checks shared by the entry points.
+bool aligned(const void* p, size_t a);
+
+}  // namespace kd

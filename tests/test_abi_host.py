@@ -1,0 +1,168 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before any HIP
+call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lm_head_top_amd as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdtopk.h")
+
+KD_OK, KD_ERR_INVALID_ARG, KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE, KD_ERR_HIP = range(5)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kd.lib_path()):
+        pytest.skip("libkdtopk.so not built")
+    return kd.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for want in ("kd_topk_kl_forward", "kd_topk_kl_backward", "kd_topk_kl_workspace_size",
+                 "kd_topk_kl_validate", "kd_status_string"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.kd_status_string(0) == b"ok"
+    assert lib.kd_status_string(3) == b"workspace too small"
+    assert lib.kd_status_string(99) == b"unknown status"
+
+
+def test_workspace_size_scales_with_chunk_not_N(lib):
+    f = kd.workspace_size
+    a = f(8192, 4096, 131072, 100, 1024)
+    b = f(32768, 4096, 131072, 100, 1024)
+    # only the 4-byte-per-row KL buffer grows with N
+    assert 0 <= b - a <= 4 * (32768 - 8192) + 512
+    c = f(8192, 4096, 131072, 100, 2048)
+    assert c > a
+    # never O(N V): the dense fp32 grid at 32K x 131072 would be 16 GiB
+    assert b < 1 << 30
+
+
+def test_workspace_size_rejects(lib):
+    f = kd.workspace_size
+    assert f(10, 12, 100, 5, 4) == 0          # D not a multiple of 8
+    assert f(10, 16, 100, 0, 4) == 0          # K = 0
+    assert f(10, 16, 100, 101, 4) == 0        # K > V
+    assert f(10, 16, 100, 5, 0) == 0          # chunk = 0
+    assert f(10, 16, 1000, 257, 4) == 0       # K > KD_MAX_K
+    assert f(10, 16, (1 << 20) + 1, 5, 4) == 0
+    assert f(-1, 16, 100, 5, 4) == 0
+    assert f(0, 16, 100, 5, 4) > 0            # empty batch is valid
+
+
+def _fwd(lib, **kw):
+    a = dict(H=8192 * 16, W=8192 * 16, idx=1 << 20, t=1 << 21, N=4, D=16, V=64, K=3, T=1.0,
+             chunk=2, loss=1 << 22, lse=1 << 23, row_kl=0, ws=1 << 24, ws_bytes=1 << 30, stream=0)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return lib.kd_topk_kl_forward(v(a["H"]), v(a["W"]), v(a["idx"]), v(a["t"]), a["N"], a["D"],
+                                  a["V"], a["K"], a["T"], a["chunk"], v(a["loss"]), v(a["lse"]),
+                                  v(a["row_kl"]), v(a["ws"]), a["ws_bytes"], v(a["stream"]))
+
+
+def _bwd(lib, **kw):
+    a = dict(H=8192 * 16, W=8192 * 16, idx=1 << 20, t=1 << 21, lse=1 << 23, g=0, N=4, D=16, V=64,
+             K=3, T=1.0, chunk=2, dH=1 << 25, dW=1 << 26, ws=1 << 24, ws_bytes=1 << 30, stream=0)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return lib.kd_topk_kl_backward(v(a["H"]), v(a["W"]), v(a["idx"]), v(a["t"]), v(a["lse"]),
+                                   v(a["g"]), a["N"], a["D"], a["V"], a["K"], a["T"], a["chunk"],
+                                   v(a["dH"]), v(a["dW"]), v(a["ws"]), a["ws_bytes"], v(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(H=0), KD_ERR_INVALID_ARG),
+    (dict(W=0), KD_ERR_INVALID_ARG),
+    (dict(idx=0), KD_ERR_INVALID_ARG),
+    (dict(t=0), KD_ERR_INVALID_ARG),
+    (dict(loss=0), KD_ERR_INVALID_ARG),
+    (dict(lse=0), KD_ERR_INVALID_ARG),
+    (dict(H=8192 * 16 + 2), KD_ERR_INVALID_ARG),      # misaligned bf16 rows
+    (dict(idx=(1 << 20) + 2), KD_ERR_INVALID_ARG),
+    (dict(row_kl=(1 << 22) + 1), KD_ERR_INVALID_ARG),
+    (dict(T=0.0), KD_ERR_INVALID_ARG),
+    (dict(T=-1.0), KD_ERR_INVALID_ARG),
+    (dict(T=float("inf")), KD_ERR_INVALID_ARG),
+    (dict(T=float("nan")), KD_ERR_INVALID_ARG),
+    (dict(N=-1), KD_ERR_INVALID_ARG),
+    (dict(D=12), KD_ERR_INVALID_ARG),
+    (dict(K=0), KD_ERR_INVALID_ARG),
+    (dict(K=65), KD_ERR_INVALID_ARG),
+    (dict(V=1000, K=300), KD_ERR_UNSUPPORTED),
+    (dict(V=(1 << 20) + 8), KD_ERR_UNSUPPORTED),
+    (dict(chunk=0), KD_ERR_INVALID_ARG),
+    (dict(ws=0), KD_ERR_WORKSPACE),
+    (dict(ws_bytes=16), KD_ERR_WORKSPACE),
+    (dict(ws=(1 << 24) + 16), KD_ERR_INVALID_ARG),
+])
+def test_forward_rejects_before_any_hip_call(lib, kw, want):
+    assert _fwd(lib, **kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dW=0), KD_ERR_INVALID_ARG),
+    (dict(dH=0), KD_ERR_INVALID_ARG),
+    (dict(lse=0), KD_ERR_INVALID_ARG),
+    (dict(dW=(1 << 26) + 4), KD_ERR_INVALID_ARG),
+    (dict(g=(1 << 27) + 2), KD_ERR_INVALID_ARG),
+    (dict(T=0.0), KD_ERR_INVALID_ARG),
+    (dict(K=65), KD_ERR_INVALID_ARG),
+    (dict(ws_bytes=1), KD_ERR_WORKSPACE),
+])
+def test_backward_rejects_before_any_hip_call(lib, kw, want):
+    assert _bwd(lib, **kw) == want
+
+
+def test_backward_empty_batch_is_a_no_op(lib):
+    # N = 0: nothing to accumulate, nothing enqueued
+    assert _bwd(lib, N=0, H=0, W=0, idx=0, t=0, lse=0, dH=0, ws=0, ws_bytes=0) == KD_OK
+
+
+def test_validate_rejects(lib):
+    v = ctypes.c_void_p
+    assert lib.kd_topk_kl_validate(v(1 << 20), 4, 3, 64, v(0), v(0)) == KD_ERR_INVALID_ARG
+    assert lib.kd_topk_kl_validate(v(1 << 20), 4, 0, 64, v(1 << 21), v(0)) == KD_ERR_INVALID_ARG
+    assert lib.kd_topk_kl_validate(v(0), 4, 3, 64, v(1 << 21), v(0)) == KD_ERR_INVALID_ARG
+
+
+def test_profile_api(lib):
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    assert lib.kd_profile_enable(1 << 8) == KD_ERR_INVALID_ARG
+    assert lib.kd_profile_read(-1, ctypes.byref(ms), ctypes.byref(n)) == KD_ERR_INVALID_ARG
+    assert lib.kd_profile_enable(0) == KD_OK
+    assert lib.kd_profile_enable(0xFF) == KD_OK
+    assert lib.kd_profile_enable(0) == KD_OK
+    assert lib.kd_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == KD_OK
+    assert n.value == 0 and ms.value == 0.0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    mod = importlib.reload(kd)
+    monkeypatch.setattr(mod, "_lib", None)
+    monkeypatch.setattr(mod, "_HERE", str(tmp_path))
+    with pytest.raises(ImportError):
+        mod.load_library()
+    monkeypatch.undo()
+    importlib.reload(kd)
