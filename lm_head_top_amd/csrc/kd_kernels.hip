@@ -589,20 +589,31 @@ __global__ __launch_bounds__(NT) void dw_kernel(DwArgs a) {
                                 a.rows, 0, a.rows, acc, smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  // Read-modify-write of the fp32 dW tile in four batches of 64 values per
+  // lane: all loads of a batch are issued before its stores, so they overlap
+  // instead of forming 256 dependent round trips.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    float old[4][16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = tn * kTile + wn * 128 + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = tm * kTile + acc_row(wm, i, r, lane);
-        if (v < a.V && d < a.D) {
-          float* dst = a.dW + int64_t(v) * a.D + d;
-          *dst += acc[i][j][r];
-        }
+        old[j][r] = (v < a.V && d < a.D) ? a.dW[int64_t(v) * a.D + d] : 0.f;
       }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = tn * kTile + wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = tm * kTile + acc_row(wm, i, r, lane);
+        if (v < a.V && d < a.D) a.dW[int64_t(v) * a.D + d] = old[j][r] + acc[i][j][r];
+      }
+    }
+  }
 }
 
 __global__ __launch_bounds__(NT) void validate_kernel(const int32_t* __restrict__ idx, int64_t N,

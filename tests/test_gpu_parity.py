@@ -89,7 +89,11 @@ def _edge_ids(V, K, N, seed):
     """Rows of K distinct ids that cover 0, V-1, every tile boundary +-1 and
     the tail tile, plus random fill."""
     edges = {0, 1, V - 1, V - 2}
-    for b in range(256, V, 256):
+    ntiles = (V + 255) // 256
+    # boundaries of the first tiles, a spread of middle tiles and the last tiles
+    for tb in sorted(set(list(range(1, 5)) + list(range(5, ntiles, 97)) +
+                         list(range(max(1, ntiles - 4), ntiles)))):
+        b = tb * 256
         edges.update({b - 1, b, b + 1})
     tail0 = (V - 1) // 256 * 256
     edges.update(range(tail0, min(V, tail0 + 8)))
