@@ -140,15 +140,17 @@ const char* kd_status_string(kd_status s);
  * clears them.
  */
 enum {
-  KD_KERNEL_PREP = 0,
-  KD_KERNEL_LOGITS_FWD = 1,
-  KD_KERNEL_COMBINE = 2,
-  KD_KERNEL_FINALIZE = 3,
-  KD_KERNEL_LOGITS_BWD = 4,
-  KD_KERNEL_DH = 5,
-  KD_KERNEL_DH_REDUCE = 6,
-  KD_KERNEL_DW = 7,
-  KD_KERNEL_COUNT = 8
+  KD_KERNEL_TEACHER = 0,    /* teacher probabilities of a chunk */
+  KD_KERNEL_LOGITS_FWD = 1, /* forward logits tile + online softmax / gather epilogue */
+  KD_KERNEL_COMBINE = 2,    /* merge of vocab-tile partials into lse and KL per row */
+  KD_KERNEL_FINALIZE = 3,   /* mean over positions */
+  KD_KERNEL_LOGITS_BWD = 4, /* recomputed logits tile + gradient epilogue */
+  KD_KERNEL_DH = 5,         /* dH = G W */
+  KD_KERNEL_DH_REDUCE = 6,  /* sum of the dH split partials */
+  KD_KERNEL_DW = 7,         /* dW += G^T H */
+  KD_KERNEL_BUCKET = 8,     /* cache entries bucketed by tile */
+  KD_KERNEL_TRANSPOSE = 9,  /* W^T and H_c^T copies for the backward GEMMs */
+  KD_KERNEL_COUNT = 10
 };
 kd_status kd_profile_enable(uint32_t kernel_mask);
 kd_status kd_profile_read(int32_t kernel_id, double* total_ms, int64_t* launches);

@@ -22,8 +22,8 @@ _LIB_NAME = "libkdtopk.so"
 _lib = None
 
 KERNELS = {
-    "prep": 0, "logits_fwd": 1, "combine": 2, "finalize": 3,
-    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7,
+    "teacher": 0, "logits_fwd": 1, "combine": 2, "finalize": 3,
+    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7, "bucket": 8, "transpose": 9,
 }
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem size",

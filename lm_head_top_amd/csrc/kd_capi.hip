@@ -104,9 +104,10 @@ kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W, const int32_t
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
     const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
     const int npt = (rows + kd::kTile - 1) / kd::kTile;
-    kd::PrepArgs pa{topk_idx + row0 * K, topk_logit + row0 * K, rows, K, int(V), int(p.nvt), invT,
-                    pw, hw, boff, ent};
-    KD_LAUNCH(KD_KERNEL_PREP, s, kd::launch_prep(pa, npt, s));
+    kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
+    KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
+    kd::BucketArgs ba{topk_idx + row0 * K, rows, K, int(V), int(p.nvt), boff, ent};
+    KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, npt, s));
     kd::LogitsArgs la{};
     la.W = W;
     la.Hc = H + row0 * D;
@@ -155,18 +156,25 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
   int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
   uint32_t* ent = reinterpret_cast<uint32_t*>(ws + p.off_ent);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
+  uint16_t* GT = reinterpret_cast<uint16_t*>(ws + p.off_gt);
+  uint16_t* WT = reinterpret_cast<uint16_t*>(ws + p.off_wt);
+  uint16_t* HT = reinterpret_cast<uint16_t*>(ws + p.off_ht);
   float* dhp = reinterpret_cast<float*>(ws + p.off_dhp);
   const float invT = 1.f / T;
   const float g_scale = float(1.0 / (double(N) * double(T)));
-  const int ktiles = int(p.Vp / 64);
+  const int ktiles = int(p.Vp / kd::gemm_bk());
   const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
 
+  // W^T [D, Vp] (zero past V) so that dH = G_c W reads vocab-contiguous rows
+  KD_LAUNCH(KD_KERNEL_TRANSPOSE, s,
+            kd::launch_transpose(W, D, int(V), int(D), WT, p.Vp, int(p.Vp), s));
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
     const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
     const int npt = (rows + kd::kTile - 1) / kd::kTile;
-    kd::PrepArgs pa{topk_idx + row0 * K, topk_logit + row0 * K, rows, K, int(V), int(p.nvt), invT,
-                    pw, hw, boff, ent};
-    KD_LAUNCH(KD_KERNEL_PREP, s, kd::launch_prep(pa, npt, s));
+    kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
+    KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
+    kd::BucketArgs ba{topk_idx + row0 * K, rows, K, int(V), int(p.nvt), boff, ent};
+    KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, npt, s));
     kd::LogitsArgs la{};
     la.W = W;
     la.Hc = H + row0 * D;
@@ -186,13 +194,18 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
     la.grad_loss = grad_loss;
     la.g_scale = g_scale;
     la.G = G;
+    la.GT = GT;
     KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
-    kd::DhArgs da{G, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
+    kd::DhArgs da{G, WT, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
     KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
     if (p.dh_split > 1)
       KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
                 kd::launch_dh_reduce(dhp, p.dh_split, rows, int(D), p.c_pad, dH + row0 * D, s));
-    kd::DwArgs wa{G, H + row0 * D, rows, int(D), int(V), p.Vp, dW};
+    // H_c^T [D, c_pad] (zero past the chunk's rows) for dW += G_c^T H_c
+    const int rpad = (rows + 63) / 64 * 64;
+    KD_LAUNCH(KD_KERNEL_TRANSPOSE, s,
+              kd::launch_transpose(H + row0 * D, D, rows, int(D), HT, p.c_pad, rpad, s));
+    kd::DwArgs wa{GT, HT, rows, int(D), int(V), p.Vp, p.c_pad, dW};
     KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
   }
   return KD_OK;

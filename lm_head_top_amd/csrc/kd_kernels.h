@@ -9,15 +9,19 @@
 
 namespace kd {
 
-// Per-chunk teacher side: p = softmax_K(t/T), h = sum p log p, and the chunk's
-// cache entries bucketed by (position tile, vocab tile).
-struct PrepArgs {
-  const int32_t* idx;   // [rows, K], already offset to the chunk's first row
-  const float* t;       // [rows, K]
-  int rows, K, V, nvt;
+// Per-chunk teacher side: p = softmax_K(t/T) and h = sum p log p per position.
+struct TeacherArgs {
+  const float* t;       // [rows, K], offset to the chunk's first row
+  int rows, K;
   float invT;
   float* p;             // [c_pad, K]
   float* h;             // [c_pad]
+};
+
+// Per-chunk cache entries bucketed by (position tile, vocab tile).
+struct BucketArgs {
+  const int32_t* idx;   // [rows, K], offset to the chunk's first row
+  int rows, K, V, nvt;
   int32_t* boff;        // [npt, nvt + 1]
   uint32_t* ent;        // [npt, kTile * K]
 };
@@ -42,6 +46,7 @@ struct LogitsArgs {
   const float* grad_loss;  // device scalar or null
   float g_scale;        // 1 / (N T)
   uint16_t* G;          // [c_pad, Vp] bf16
+  uint16_t* GT;         // [Vp, c_pad] bf16 (transpose of G)
 };
 
 struct CombineArgs {
@@ -58,7 +63,7 @@ struct CombineArgs {
 
 struct DhArgs {
   const uint16_t* G;   // [c_pad, Vp]
-  const uint16_t* W;   // [V, D]
+  const uint16_t* WT;  // [D, Vp] (transpose of W, zero past V)
   int rows, D, V;
   int64_t Vp;
   int split;           // number of K splits
@@ -69,14 +74,18 @@ struct DhArgs {
 };
 
 struct DwArgs {
-  const uint16_t* G;   // [c_pad, Vp]
-  const uint16_t* Hc;  // [rows, D] offset to the chunk
+  const uint16_t* GT;  // [Vp, c_pad] (zero past the chunk's rows)
+  const uint16_t* HT;  // [D, c_pad] transpose of H_c (zero past the chunk's rows)
   int rows, D, V;
-  int64_t Vp;
+  int64_t Vp, c_pad;
   float* dW;           // [V, D]
 };
 
-hipError_t launch_prep(const PrepArgs& a, int npt, hipStream_t s);
+int gemm_bk();  // K depth of one GEMM pipeline stage
+hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s);
+hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s);
+hipError_t launch_transpose(const uint16_t* src, int64_t ld_src, int R, int C, uint16_t* dst,
+                            int64_t ld_dst, int Rpad, hipStream_t s);
 hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -6,47 +6,67 @@
 // loss and drop them; the backward recomputes each chunk's logits.  Here every
 // chunk runs as
 //
-//   prep      teacher probabilities p = softmax_K(t/T), h = sum p log p, and the
-//             chunk's (row, id, k) cache entries bucketed by (position tile,
-//             vocab tile) so that each logits tile finds its own entries;
+//   teacher   p = softmax_K(t/T) and h = sum p log p per position (one wave per row);
+//   bucket    the chunk's (row, id, k) cache entries, counting-sorted by (position
+//             tile, vocab tile) so each logits tile finds exactly its own entries;
 //   logits    z^T = W H_c^T / T for one 256 x 256 (vocab, position) tile on bf16
-//             MFMA (v_mfma_f32_32x32x16_bf16) with LDS-staged operands, then
+//             MFMA (v_mfma_f32_32x32x16_bf16), then
 //             forward: per-position tile max / sum-exp and the logits at the
-//                      cached ids (never the tile itself) go to small buffers;
+//                      cached ids go to small buffers (never the tile itself);
 //             backward: G = g/(N T) (exp(z - lse) - p scattered at the ids),
-//                      rounded to bf16 into the chunk's G_c[c, V];
+//                      rounded to bf16 into G_c[c, V] and its transpose G_c^T;
 //   combine   forward: merge the vocab-tile partials into lse and KL per row;
 //   dh / dw   dH_c = G_c W (split over V, fp32 partials) and dW += G_c^T H_c.
 //
-// All four GEMMs share one MFMA main loop: 256 threads (2 x 2 waves of 64),
-// a 256 x 256 output tile with a 128 x 128 tile per wave held as 4 x 4 MFMA
-// 32x32 accumulators, K steps of 64 through double-buffered LDS.  Operands
-// whose K axis is contiguous in memory are copied to LDS as 16-byte vectors;
-// operands whose M/N axis is contiguous are transposed 8 x 8 in registers on
-// the way in, so the LDS layout (K contiguous, 144-byte rows) and the MFMA
-// reads are the same for both.
+// GEMM core: 256 threads (2 x 2 waves of 64), a 256 x 256 output tile with a
+// 128 x 128 tile per wave held as 4 x 4 MFMA 32x32 fp32 accumulators.  Both
+// operands are K-contiguous in memory (the backward keeps W^T, H_c^T and
+// G_c^T copies so that every GEMM reads K-contiguous rows).  Tiles of BK
+// columns stream from HBM straight into LDS with buffer_load_dwordx4 ... lds
+// (no register staging; out-of-range rows and columns read as zero), through
+// a ring of STAGES buffers.  Inside a row of the LDS tile the 16-byte chunks
+// are XOR-swizzled by row so the MFMA fragment reads (ds_read_b128, lanes on
+// 32 consecutive rows at one k offset) hit distinct banks.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "kd_kernels.h"
 
+#ifndef KD_BK
+#define KD_BK 64
+#endif
+#ifndef KD_STAGES
+#define KD_STAGES 2
+#endif
+
 namespace kd {
 namespace {
 
-constexpr int NT = 256;                       // threads per workgroup
-constexpr int BK = 64;                        // K step
-constexpr int LDK = BK + 8;                   // LDS row stride (bf16): 144 B, conflict-free 16 B reads
-constexpr int OPER = kTile * LDK;             // bf16 elements per operand per stage
-constexpr int SMEM_ELEMS = 4 * OPER;          // 2 stages x 2 operands
-constexpr int SLD = kTile + 4;                // fp32 row stride of the epilogue staging tile
-constexpr int STAGE_FLOATS = 128 * SLD;       // half a tile: 128 positions x 256 vocab
+constexpr int NT = 256;                          // threads per GEMM workgroup
+constexpr int BK = KD_BK;                        // K columns per pipeline stage
+constexpr int STAGES = KD_STAGES;                // LDS ring depth
+constexpr int CH = BK / 8;                       // 16-byte chunks per LDS row
+constexpr int ROWB = BK * 2;                     // bytes per LDS row
+constexpr int RPI = 64 / CH;                     // rows covered by one 1 KiB direct load
+constexpr int NI = kTile * ROWB / 1024 / 4;      // direct loads per wave, per operand, per stage
+constexpr int OPER_BYTES = kTile * ROWB;         // one operand tile in LDS
+constexpr int STAGE_BYTES = 2 * OPER_BYTES;
+constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
+constexpr int SLD = kTile + 4;                   // fp32 row stride of the epilogue staging tile
+constexpr int STAGE_FLOATS = 128 * SLD;          // half a tile: 128 positions x 256 vocab
+constexpr int EPI_BYTES = (STAGE_FLOATS + 4 * kTile) * 4;
+constexpr int SMEM_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+constexpr uint32_t kOOB = 0xFFFFFFF0u;           // buffer offset past any operand: reads return 0
 constexpr float LOG2E = 1.4426950408889634f;
 
-static_assert((STAGE_FLOATS + 4 * kTile) * 4 <= SMEM_ELEMS * 2, "epilogue staging must fit in LDS");
+static_assert(BK == 32 || BK == 64, "BK");
+static_assert(STAGES >= 2, "STAGES");
+static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -90,109 +110,114 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return x * per + (x < rem ? x : rem) + i;
 }
 
-// ---------------------------------------------------------------- loaders ---
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-// Operand stored K-contiguous: X[mn][k] with leading dimension ld.  A 256 x 64
-// tile is 2048 16-byte vectors, 8 per thread.  Requires k_lim % 8 == 0.
-struct LoadKC {
-  uint4 r[8];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ X, int64_t ld, int mn0,
-                                       int mn_lim, int k0, int k_lim) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int v = i * NT + t;
-      const int row = v >> 3, kk = (v & 7) * 8;
-      const int mn = mn0 + row, k = k0 + kk;
-      if (mn < mn_lim && k < k_lim)
-        r[i] = *reinterpret_cast<const uint4*>(X + int64_t(mn) * ld + k);
-      else
-        r[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int v = i * NT + t;
-      const int row = v >> 3, kk = (v & 7) * 8;
-      *reinterpret_cast<uint4*>(s + row * LDK + kk) = r[i];
-    }
-  }
-};
+// Workgroup barrier that orders LDS accesses for the compiler but does not wait
+// for outstanding loads (the LDS ring is managed with explicit vmcnt waits).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Operand stored M/N-contiguous: X[k][mn] with leading dimension ld.  Thread t
-// owns the 8 x 8 block (k = kb*8.., mn = mb*8..) with kb = t % 8, mb = t / 8,
-// loads it as 8 row vectors and writes it transposed (8 K-contiguous vectors).
-// Requires mn_lim % 8 == 0.
-struct LoadMC {
-  uint4 r[8];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ X, int64_t ld, int mn0,
-                                       int mn_lim, int k0, int k_lim) {
-    const int t = threadIdx.x;
-    const int kb = t & 7, mb = t >> 3;
-    const int mn = mn0 + mb * 8;
+// XOR swizzle of the 16-byte chunks of LDS row r.
+__device__ __forceinline__ int swz(int r) { return CH == 8 ? (r & 7) : ((r >> 1) & 3); }
+
+// ------------------------------------------------------ direct LDS loads ---
+
+// Streams a 256-row, K-contiguous operand X[row][k] (leading dimension ld,
+// elements) into LDS tiles of 256 x BK.  Each wave issues NI direct loads of
+// 1 KiB; lane l of load j fills LDS row (wave*NI + j)*RPI + l/CH, physical
+// chunk l%CH, with logical chunk (l%CH) ^ swz(row).  Rows at or past row_lim
+// and columns at or past k_lim read as zero.
+struct DLoad {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[NI];
+  int kc;  // first k of this lane's chunk within a tile
+
+  __device__ __forceinline__ void init(const uint16_t* base, uint64_t bytes, int64_t ld, int row0,
+                                       int row_lim) {
+    const uint32_t nrec = bytes < uint64_t(kOOB) ? uint32_t(bytes) : kOOB;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, int(nrec), 0x00020000);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rib = lane / CH, phys = lane % CH;
+    kc = (phys ^ swz(rib)) * 8;  // block rows start at multiples of RPI: swz(row) == swz(rib)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = k0 + kb * 8 + j;
-      if (mn < mn_lim && k < k_lim)
-        r[j] = *reinterpret_cast<const uint4*>(X + int64_t(k) * ld + mn);
-      else
-        r[j] = make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < NI; ++j) {
+      const int row = row0 + (wave * NI + j) * RPI + rib;
+      voff[j] = row < row_lim ? uint32_t((int64_t(row) * ld + kc) * 2) : kOOB;
     }
   }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-    const int t = threadIdx.x;
-    const int kb = t & 7, mb = t >> 3;
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(r);  // w[j*4 + q]: row j, elements 2q, 2q+1
+
+  __device__ __forceinline__ void issue(char* stage, int k0, int k_lim) const {
+    const int wave = threadIdx.x >> 6;
+    const bool kok = k0 + kc < k_lim;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int q = c >> 1;
-      uint32_t o[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t x = w[(2 * d) * 4 + q], y = w[(2 * d + 1) * 4 + q];
-        o[d] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-      }
-      *reinterpret_cast<uint4*>(s + (mb * 8 + c) * LDK + kb * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t off = (kok && voff[j] != kOOB) ? voff[j] + uint32_t(k0) * 2u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_void*)(stage + (wave * NI + j) * 1024), 16, off, 0, 0, 0);
     }
   }
 };
 
-// ------------------------------------------------------------- main loop ---
+// --------------------------------------------------------------- MFMA core ---
 
-// One 64-deep K step of the wave's 128 x 128 tile from LDS.
-// MFMA 32x32x16 operand layout: lane l supplies row (l % 32) and the 8
-// consecutive k values 8 * (l / 32) .. +7 of A, and the same for B's column.
-__device__ __forceinline__ void mma_step(const uint16_t* __restrict__ sA,
-                                         const uint16_t* __restrict__ sB, f32x16 (&acc)[4][4],
-                                         int wm, int wn, int lane) {
+// One BK-deep stage of the wave's 128 x 128 tile.  MFMA 32x32x16 operands:
+// lane l supplies row l % 32 and the 8 consecutive k of half l / 32.
+// Fragments of the next 16-deep step load while the current step multiplies.
+__device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const char* __restrict__ sB,
+                                          f32x16 (&acc)[4][4], int wm, int wn, int lane) {
+  constexpr int NS = BK / 16;
+  const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31);  // tile rows are r31 mod 32
+  const char* pa = sA + (wm * 128 + r31) * ROWB;
+  const char* pb = sB + (wn * 128 + r31) * ROWB;
+  bf16x8 fa[2][4], fb[2][4];
+  {
+    const int off = (hi ^ sw) * 16;
 #pragma unroll
-  for (int kk = 0; kk < BK; kk += 16) {
-    bf16x8 a[4], b[4];
-    const int koff = kk + (lane >> 5) * 8;
+    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 128 + i * 32 + (lane & 31)) * LDK + koff);
+    for (int j = 0; j < 4; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + off);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the first step's 8 fragment reads
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(sB + (wn * 128 + j * 32 + (lane & 31)) * LDK + koff);
+  for (int s = 0; s < NS; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < NS) {
+      const int off = ((2 * (s + 1) + hi) ^ sw) * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[cur ^ 1][j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + off);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+    // keep the MFMA pipe fed: the next step's fragment reads go out between
+    // this step's first 8 MFMAs, so their LDS latency hides under the rest
+    if (s + 1 < NS) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    }
   }
 }
 
 // acc[i][j] (wave (wm, wn)) register r holds C[m][n] with
 //   m = wm*128 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*128 + j*32 + lane%32.
-template <class LA, class LB>
-__device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, int64_t lda, int a_mn0,
-                                              int a_mn_lim, int a_k_lim,
-                                              const uint16_t* __restrict__ B, int64_t ldb, int b_mn0,
-                                              int b_mn_lim, int b_k_lim, int k_begin, int k_end,
-                                              f32x16 (&acc)[4][4], uint16_t* smem) {
+__device__ __forceinline__ void gemm_core(const DLoad& la, const DLoad& lb, int k_begin, int k_end,
+                                          int ka_lim, int kb_lim, f32x16 (&acc)[4][4], char* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -203,33 +228,30 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (k_end - k_begin + BK - 1) / BK;
   if (nk <= 0) return;
-  const int ak = a_k_lim < k_end ? a_k_lim : k_end;
-  const int bk = b_k_lim < k_end ? b_k_lim : k_end;
-  LA la;
-  LB lb;
-  la.load(A, lda, a_mn0, a_mn_lim, k_begin, ak);
-  lb.load(B, ldb, b_mn0, b_mn_lim, k_begin, bk);
-  la.store(smem);
-  lb.store(smem + OPER);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) {
+      char* st = smem + s * STAGE_BYTES;
+      la.issue(st, k_begin + s * BK, ka_lim);
+      lb.issue(st + OPER_BYTES, k_begin + s * BK, kb_lim);
+    }
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const uint16_t* sA = smem + cur * 2 * OPER;
-    const uint16_t* sB = sA + OPER;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = k_begin + (kt + 1) * BK;
-      la.load(A, lda, a_mn0, a_mn_lim, k0, ak);
-      lb.load(B, ldb, b_mn0, b_mn_lim, k0, bk);
+    // stage kt has landed once only the newer stages' loads may be in flight
+    if (kt + STAGES - 2 < nk)
+      wait_vmcnt<(STAGES - 2) * 2 * NI>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    const int nxt = kt + STAGES - 1;
+    if (nxt < nk) {  // refill the buffer every wave finished reading last iteration
+      char* st = smem + (nxt % STAGES) * STAGE_BYTES;
+      la.issue(st, k_begin + nxt * BK, ka_lim);
+      lb.issue(st + OPER_BYTES, k_begin + nxt * BK, kb_lim);
     }
-    mma_step(sA, sB, acc, wm, wn, lane);
-    if (more) {
-      uint16_t* nA = smem + (cur ^ 1) * 2 * OPER;
-      la.store(nA);
-      lb.store(nA + OPER);
-    }
-    __syncthreads();
+    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    mma_stage(st, st + OPER_BYTES, acc, wm, wn, lane);
   }
+  lds_barrier();  // every wave is done with the ring before the epilogue reuses LDS
 }
 
 // Row (within the 256-row tile) of accumulator register r of block i.
@@ -254,69 +276,80 @@ __device__ __forceinline__ void stage_half(float* S, const f32x16 (&acc)[4][4], 
   }
 }
 
-// ---------------------------------------------------------------- kernels ---
+// ---------------------------------------------------------- teacher side ---
 
-__global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
+// p = softmax over the K cached teacher logits at temperature T, and
+// h = sum_k p log p (0 log 0 = 0); one wave per position.
+__global__ __launch_bounds__(NT) void teacher_kernel(TeacherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * (NT / 64) + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int K = a.K;
+  float av[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = lane + 64 * u;
+    av[u] = k < K ? a.t[row * K + k] * a.invT : -INFINITY;
+    mx = fmaxf(mx, av[u]);
+  }
+  mx = wave_max(mx);
+  float e[4], se = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    e[u] = mx == -INFINITY ? 0.f : exp2_fast((av[u] - mx) * LOG2E);
+    se += e[u];
+  }
+  se = wave_sum(se);
+  const float lnorm = mx + logf(se);
+  float hs = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = lane + 64 * u;
+    if (k < K) {
+      const float pk = se > 0.f ? e[u] / se : 0.f;
+      a.p[row * K + k] = pk;
+      if (pk > 0.f) hs += pk * (av[u] - lnorm);
+    }
+  }
+  hs = wave_sum(hs);
+  if (lane == 0) a.h[row] = hs;
+}
+
+// Counting sort of one position tile's cache entries by vocab tile.  Entry
+// word: row-in-tile << 16 | id % 256 << 8 | k.  Ids outside [0, V) are dropped.
+constexpr int BT = 1024;  // threads of the bucketing kernel
+__global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   __shared__ int cnt[kMaxVocabTiles];
-  __shared__ int part[NT];
-  const int pt = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int part[BT];
+  const int pt = blockIdx.x, tid = threadIdx.x;
   const int r0 = pt * kTile;
   const int nr = min(kTile, a.rows - r0);
-  const int K = a.K;
-
-  // teacher distribution renormalised over the K cached logits at temperature T
-  for (int rr = wave; rr < nr; rr += NT / 64) {
-    const int64_t row = r0 + rr;
-    float av[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = lane + 64 * u;
-      av[u] = k < K ? a.t[row * K + k] * a.invT : -INFINITY;
-      mx = fmaxf(mx, av[u]);
-    }
-    mx = wave_max(mx);
-    float e[4], se = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      e[u] = mx == -INFINITY ? 0.f : exp2_fast((av[u] - mx) * LOG2E);
-      se += e[u];
-    }
-    se = wave_sum(se);
-    const float lnorm = mx + logf(se);
-    float hs = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = lane + 64 * u;
-      if (k < K) {
-        const float pk = se > 0.f ? e[u] / se : 0.f;
-        a.p[row * K + k] = pk;
-        if (pk > 0.f) hs += pk * (av[u] - lnorm);
-      }
-    }
-    hs = wave_sum(hs);
-    if (lane == 0) a.h[row] = hs;
-  }
-
-  // bucket the tile's entries by vocab tile (counting sort in LDS)
-  const int nvt = a.nvt;
-  for (int v = tid; v < nvt; v += NT) cnt[v] = 0;
-  __syncthreads();
+  const int K = a.K, nvt = a.nvt;
   const int ne = nr * K;
   const int32_t* idx = a.idx + int64_t(r0) * K;
-  for (int e = tid; e < ne; e += NT) {
-    const int id = idx[e];
-    if (unsigned(id) < unsigned(a.V)) atomicAdd(&cnt[id >> 8], 1);
+  for (int v = tid; v < nvt; v += BT) cnt[v] = 0;
+  __syncthreads();
+  for (int e0 = 0; e0 < ne; e0 += 4 * BT) {
+    int id[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * BT + tid;
+      id[u] = e < ne ? idx[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (unsigned(id[u]) < unsigned(a.V)) atomicAdd(&cnt[id[u] >> 8], 1);
   }
   __syncthreads();
-  const int seg = (nvt + NT - 1) / NT;
+  const int seg = (nvt + BT - 1) / BT;
   const int b0 = tid * seg;
   int loc = 0;
   for (int q = 0; q < seg; ++q)
     if (b0 + q < nvt) loc += cnt[b0 + q];
   part[tid] = loc;
   __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
+  for (int off = 1; off < BT; off <<= 1) {
     const int x = tid >= off ? part[tid - off] : 0;
     __syncthreads();
     part[tid] += x;
@@ -333,22 +366,32 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
       run += c;
     }
   }
-  if (tid == NT - 1) bo[nvt] = part[NT - 1];
+  if (tid == BT - 1) bo[nvt] = part[BT - 1];
   __syncthreads();
   uint32_t* ent = a.ent + int64_t(pt) * kTile * K;
-  for (int e = tid; e < ne; e += NT) {
-    const int id = idx[e];
-    if (unsigned(id) < unsigned(a.V)) {
-      const int rr = e / K, k = e - rr * K;
-      const int pos = atomicAdd(&cnt[id >> 8], 1);
-      ent[pos] = (uint32_t(rr) << 16) | (uint32_t(id & (kTile - 1)) << 8) | uint32_t(k);
+  for (int e0 = 0; e0 < ne; e0 += 4 * BT) {
+    int id[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * BT + tid;
+      id[u] = e < ne ? idx[e] : -1;
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (unsigned(id[u]) < unsigned(a.V)) {
+        const int e = e0 + u * BT + tid;
+        const int rr = e / K, k = e - rr * K;
+        const int pos = atomicAdd(&cnt[id[u] >> 8], 1);
+        ent[pos] = (uint32_t(rr) << 16) | (uint32_t(id[u] & (kTile - 1)) << 8) | uint32_t(k);
+      }
   }
 }
 
+// ----------------------------------------------------------- logits tile ---
+
 template <int MODE>  // 0: forward epilogue, 1: backward epilogue
-__global__ __launch_bounds__(NT) void logits_kernel(LogitsArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void logits_kernel(LogitsArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   const int total = a.nvt * a.npt;
   const int tile = xcd_remap(blockIdx.x, total);
   const int vt = tile / a.npt, pt = tile - vt * a.npt;
@@ -357,8 +400,13 @@ __global__ __launch_bounds__(NT) void logits_kernel(LogitsArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
 
   f32x16 acc[4][4];
-  // A = W rows (vocab), B = H_c rows (positions); both K(=D)-contiguous.
-  gemm_mainloop<LoadKC, LoadKC>(a.W, a.D, v0, a.V, a.D, a.Hc, a.D, p0, a.rows, a.D, 0, a.D, acc, smem);
+  {
+    // A = W rows (vocab), B = H_c rows (positions); both D-contiguous
+    DLoad la, lb;
+    la.init(a.W, uint64_t(a.V) * a.D * 2, a.D, v0, a.V);
+    lb.init(a.Hc, uint64_t(a.rows) * a.D * 2, a.D, p0, a.rows);
+    gemm_core(la, lb, 0, a.D, a.D, a.D, acc, smem);
+  }
 
   float* S = reinterpret_cast<float*>(smem);
   float* red = S + STAGE_FLOATS;  // [4][256]
@@ -459,7 +507,7 @@ __global__ __launch_bounds__(NT) void logits_kernel(LogitsArgs a) {
         }
       }
       __syncthreads();
-      // round to bf16 and write 128 rows x 256 vocab of G_c
+      // G_c rows: 128 positions x 256 vocab, bf16
 #pragma unroll 4
       for (int it = 0; it < 16; ++it) {
         const int pl = it * 8 + (tid >> 5);
@@ -476,10 +524,23 @@ __global__ __launch_bounds__(NT) void logits_kernel(LogitsArgs a) {
           *reinterpret_cast<uint4*>(a.G + int64_t(prow) * a.Vp + v0 + c8) = o;
         }
       }
+      // G_c^T rows: 256 vocab x 128 positions, bf16 (positions past the chunk are 0)
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const float* col = S + (it * 8) * SLD + tid;
+        uint4 o;
+        o.x = bf16_rne(col[0]) | (bf16_rne(col[SLD]) << 16);
+        o.y = bf16_rne(col[2 * SLD]) | (bf16_rne(col[3 * SLD]) << 16);
+        o.z = bf16_rne(col[4 * SLD]) | (bf16_rne(col[5 * SLD]) << 16);
+        o.w = bf16_rne(col[6 * SLD]) | (bf16_rne(col[7 * SLD]) << 16);
+        *reinterpret_cast<uint4*>(a.GT + int64_t(v0 + tid) * a.c_pad + p0 + h * 128 + it * 8) = o;
+      }
       __syncthreads();
     }
   }
 }
+
+// ----------------------------------------------------------------- combine ---
 
 __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   __shared__ float sm[8][32], ss[8][32], sg[8][32];
@@ -522,8 +583,50 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const float* __restrict__ 
   if (tid == 0) loss[0] = N > 0 ? float(red[0] / double(N)) : 0.f;
 }
 
-__global__ __launch_bounds__(NT) void dh_kernel(DhArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+// --------------------------------------------------------------- transpose ---
+
+// dst[c][r] = src[r][c] for r < R, c < C; dst[c][r] = 0 for R <= r < Rpad.
+// 64 x 64 tiles through LDS.  C % 8 == 0, Rpad % 64 == 0, ld % 8 == 0.
+__global__ __launch_bounds__(NT) void transpose_kernel(const uint16_t* __restrict__ src, int64_t lds_,
+                                                       int R, int C, uint16_t* __restrict__ dst,
+                                                       int64_t ldd, int Rpad) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = u * NT + tid;  // 512 chunks of 8 elements
+    const int rr = q >> 3, cc = (q & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + int64_t(r) * lds_ + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[rr][cc + 2 * e] = uint16_t(w[e] & 0xffffu);
+      tile[rr][cc + 2 * e + 1] = uint16_t(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = u * NT + tid;
+    const int cc = q >> 3, rr = (q & 7) * 8;
+    const int c = c0 + cc, r = r0 + rr;
+    if (c < C && r < Rpad) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = uint32_t(tile[rr + 2 * e][cc]) | (uint32_t(tile[rr + 2 * e + 1][cc]) << 16);
+      *reinterpret_cast<uint4*>(dst + int64_t(c) * ldd + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// --------------------------------------------------------------- dH and dW ---
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void dh_kernel(DhArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[MAIN_BYTES];
   const int tiles_m = (a.rows + kTile - 1) / kTile;
   const int tiles_n = (a.D + kTile - 1) / kTile;
   const int tiles = tiles_m * tiles_n;
@@ -534,9 +637,13 @@ __global__ __launch_bounds__(NT) void dh_kernel(DhArgs a) {
   int k_end = k_begin + a.ktiles_per_split * BK;
   if (k_end > a.Vp) k_end = int(a.Vp);
   f32x16 acc[4][4];
-  // A = G_c (positions x vocab, vocab-contiguous), B = W (vocab x D, D-contiguous)
-  gemm_mainloop<LoadKC, LoadMC>(a.G, a.Vp, tm * kTile, a.rows, int(a.Vp), a.W, a.D, tn * kTile, a.D,
-                                a.V, k_begin, k_end, acc, smem);
+  {
+    // A = G_c (positions x vocab), B = W^T (D x vocab); both vocab-contiguous
+    DLoad la, lb;
+    la.init(a.G, uint64_t(a.c_pad) * a.Vp * 2, a.Vp, tm * kTile, a.rows);
+    lb.init(a.WT, uint64_t(a.D) * a.Vp * 2, a.Vp, tn * kTile, a.D);
+    gemm_core(la, lb, k_begin, k_end, int(a.Vp), int(a.Vp), acc, smem);
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -577,44 +684,56 @@ __global__ __launch_bounds__(NT) void dh_reduce_kernel(const float* __restrict__
   reinterpret_cast<uint2*>(dH)[i] = o;
 }
 
-__global__ __launch_bounds__(NT) void dw_kernel(DwArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void dw_kernel(DwArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[MAIN_BYTES];
   const int tiles_m = int((a.V + kTile - 1) / kTile);
   const int tiles_n = (a.D + kTile - 1) / kTile;
   const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int kext = (a.rows + BK - 1) / BK * BK;  // both operands are zero past the chunk's rows
   f32x16 acc[4][4];
-  // A[v][p] = G_c[p][v] (vocab-contiguous), B[p][d] = H_c[p][d] (D-contiguous)
-  gemm_mainloop<LoadMC, LoadMC>(a.G, a.Vp, tm * kTile, int(a.Vp), a.rows, a.Hc, a.D, tn * kTile, a.D,
-                                a.rows, 0, a.rows, acc, smem);
+  {
+    // A = G_c^T (vocab x positions), B = H_c^T (D x positions); both position-contiguous
+    DLoad la, lb;
+    la.init(a.GT, uint64_t(a.Vp) * a.c_pad * 2, a.c_pad, tm * kTile, a.V);
+    lb.init(a.HT, uint64_t(a.D) * a.c_pad * 2, a.c_pad, tn * kTile, a.D);
+    gemm_core(la, lb, 0, kext, kext, kext, acc, smem);
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // Read-modify-write of the fp32 dW tile in four batches of 64 values per
-  // lane: all loads of a batch are issued before its stores, so they overlap
-  // instead of forming 256 dependent round trips.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float old[4][16];
+  // Read-modify-write of the fp32 dW tile, software-pipelined over the four
+  // row blocks i: the old values of block i + 1 are loaded before block i is
+  // stored (the blocks are disjoint rows), so two batches of 64 loads per
+  // lane stay in flight instead of one.
+  float old[2][4][16];
+  auto load_block = [&](int i, float (&o)[4][16]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = tn * kTile + wn * 128 + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = tm * kTile + acc_row(wm, i, r, lane);
-        old[j][r] = (v < a.V && d < a.D) ? a.dW[int64_t(v) * a.D + d] : 0.f;
+        o[j][r] = (v < a.V && d < a.D) ? a.dW[int64_t(v) * a.D + d] : 0.f;
       }
     }
+  };
+  load_block(0, old[0]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i + 1 < 4) load_block(i + 1, old[(i + 1) & 1]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = tn * kTile + wn * 128 + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = tm * kTile + acc_row(wm, i, r, lane);
-        if (v < a.V && d < a.D) a.dW[int64_t(v) * a.D + d] = old[j][r] + acc[i][j][r];
+        if (v < a.V && d < a.D) a.dW[int64_t(v) * a.D + d] = old[i & 1][j][r] + acc[i][j][r];
       }
     }
   }
 }
+
+// ---------------------------------------------------------------- utility ---
 
 __global__ __launch_bounds__(NT) void validate_kernel(const int32_t* __restrict__ idx, int64_t N,
                                                       int K, int64_t V, int32_t* flags) {
@@ -644,8 +763,15 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-hipError_t launch_prep(const PrepArgs& a, int npt, hipStream_t s) {
-  hipLaunchKernelGGL(prep_kernel, dim3(npt), dim3(NT), 0, s, a);
+int gemm_bk() { return BK; }
+
+hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(teacher_kernel, dim3(unsigned(ceil_div(a.rows, NT / 64))), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s) {
+  hipLaunchKernelGGL(bucket_kernel, dim3(npt), dim3(BT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -666,6 +792,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 
 hipError_t launch_finalize(const float* rowkl, int64_t N, float* loss, hipStream_t s) {
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(NT), 0, s, rowkl, N, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint16_t* src, int64_t ld_src, int R, int C, uint16_t* dst,
+                            int64_t ld_dst, int Rpad, hipStream_t s) {
+  hipLaunchKernelGGL(transpose_kernel, dim3(unsigned(ceil_div(C, 64)), unsigned(ceil_div(Rpad, 64))),
+                     dim3(NT), 0, s, src, ld_src, R, C, dst, ld_dst, Rpad);
   return hipGetLastError();
 }
 
