@@ -136,13 +136,14 @@ def main():
 
     dom = max(GEMM_KERNELS, key=lambda k: per_kernel[k]["total_ms"])
     dk = per_kernel[dom]
-    # every GEMM kernel launch covers one chunk: 2 * rows * D * V flops
+    # each GEMM kind does 2 N D V flops per step in total, spread over its launches
     flops_dom = 2.0 * cfg.N * cfg.D * cfg.V * args.steps
-    achieved = flops_dom / (dk["total_ms"] * 1e-3) / 1e12
+    per_launch = flops_dom / max(dk["launches"], 1)
+    achieved = per_launch / (dk["avg_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": None, "avg_launch_ms": round(dk["avg_ms"], 4),
-                "flops_per_launch": 2.0 * min(cfg.chunk, cfg.N) * cfg.D * cfg.V}
+                "flops_per_launch": per_launch}
 
     base = None
     if args.cpu_rows > 0:

@@ -168,6 +168,11 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
   // W^T [D, Vp] (zero past V) so that dH = G_c W reads vocab-contiguous rows
   KD_LAUNCH(KD_KERNEL_TRANSPOSE, s,
             kd::launch_transpose(W, D, int(V), int(D), WT, p.Vp, int(p.Vp), s));
+  // G_c^T and H_c^T of up to dw_group chunks sit side by side (ld = group *
+  // c_pad) and feed one dW GEMM with K = the group's positions.
+  const int64_t gt_ld = int64_t(p.dw_group) * p.c_pad;
+  const int bk = kd::gemm_bk();
+  int gj = 0;
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
     const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
     const int npt = (rows + kd::kTile - 1) / kd::kTile;
@@ -195,18 +200,26 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
     la.g_scale = g_scale;
     la.G = G;
     la.GT = GT;
+    la.gt_ld = gt_ld;
+    la.gt_col0 = int64_t(gj) * p.c_pad;
     KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
     kd::DhArgs da{G, WT, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
     KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
     if (p.dh_split > 1)
       KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
                 kd::launch_dh_reduce(dhp, p.dh_split, rows, int(D), p.c_pad, dH + row0 * D, s));
-    // H_c^T [D, c_pad] (zero past the chunk's rows) for dW += G_c^T H_c
-    const int rpad = (rows + 63) / 64 * 64;
+    // H_c^T [D, c_pad] (zero past the chunk's rows) next to the group's others
     KD_LAUNCH(KD_KERNEL_TRANSPOSE, s,
-              kd::launch_transpose(H + row0 * D, D, rows, int(D), HT, p.c_pad, rpad, s));
-    kd::DwArgs wa{GT, HT, rows, int(D), int(V), p.Vp, p.c_pad, dW};
-    KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
+              kd::launch_transpose(H + row0 * D, D, rows, int(D), HT + int64_t(gj) * p.c_pad, gt_ld,
+                                   int(p.c_pad), s));
+    ++gj;
+    const bool last = row0 + p.chunk >= N;
+    if (gj == p.dw_group || last) {
+      const int kext = int((gj - 1) * p.c_pad + (rows + bk - 1) / bk * bk);
+      kd::DwArgs wa{GT, HT, kext, int(D), int(V), p.Vp, gt_ld, dW};
+      KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
+      gj = 0;
+    }
   }
   return KD_OK;
 }

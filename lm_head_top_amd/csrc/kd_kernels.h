@@ -46,7 +46,8 @@ struct LogitsArgs {
   const float* grad_loss;  // device scalar or null
   float g_scale;        // 1 / (N T)
   uint16_t* G;          // [c_pad, Vp] bf16
-  uint16_t* GT;         // [Vp, c_pad] bf16 (transpose of G)
+  uint16_t* GT;         // [Vp, gt_ld] bf16: G^T of the chunk at columns gt_col0 ..
+  int64_t gt_ld, gt_col0;
 };
 
 struct CombineArgs {
@@ -73,11 +74,13 @@ struct DhArgs {
   int64_t c_pad;
 };
 
+// dW += G^T H over a group of chunks whose G^T and H^T sit side by side.
 struct DwArgs {
-  const uint16_t* GT;  // [Vp, c_pad] (zero past the chunk's rows)
-  const uint16_t* HT;  // [D, c_pad] transpose of H_c (zero past the chunk's rows)
-  int rows, D, V;
-  int64_t Vp, c_pad;
+  const uint16_t* GT;  // [Vp, ld] (zero past the group's rows within kext)
+  const uint16_t* HT;  // [D, ld]
+  int kext;            // positions of the group, rounded up to the GEMM K step
+  int D, V;
+  int64_t Vp, ld;
   float* dW;           // [V, D]
 };
 

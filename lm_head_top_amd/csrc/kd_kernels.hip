@@ -18,8 +18,10 @@
 //   combine   forward: merge the vocab-tile partials into lse and KL per row;
 //   dh / dw   dH_c = G_c W (split over V, fp32 partials) and dW += G_c^T H_c.
 //
-// GEMM core: 256 threads (2 x 2 waves of 64), a 256 x 256 output tile with a
-// 128 x 128 tile per wave held as 4 x 4 MFMA 32x32 fp32 accumulators.  Both
+// GEMM core: 512 threads (2 x 4 waves of 64, two waves per SIMD), a 256 x 256
+// output tile with a 128 x 64 tile per wave held as 4 x 2 MFMA 32x32 fp32
+// accumulators.  A wave that stalls issuing a load leaves its SIMD to the
+// other wave's MFMAs.  Both
 // operands are K-contiguous in memory (the backward keeps W^T, H_c^T and
 // G_c^T copies so that every GEMM reads K-contiguous rows).  Tiles of BK
 // columns stream from HBM straight into LDS with buffer_load_dwordx4 ... lds
@@ -39,20 +41,29 @@
 #ifndef KD_STAGES
 #define KD_STAGES 2
 #endif
+#ifndef KD_LPS
+#define KD_LPS 4
+#endif
 
 namespace kd {
 namespace {
 
-constexpr int NT = 256;                          // threads per GEMM workgroup
+constexpr int NT = 256;                          // threads of the small kernels
+constexpr int GT = 512;                          // threads per GEMM workgroup: 8 waves, 2 per SIMD
+constexpr int WAVES = GT / 64;
+constexpr int WT_N = 64;                         // wave tile: 128 (M) x 64 (N), waves 2 (M) x 4 (N)
+constexpr int NJ = WT_N / 32;                    // 32-wide MFMA blocks per wave along N
 constexpr int BK = KD_BK;                        // K columns per pipeline stage
 constexpr int STAGES = KD_STAGES;                // LDS ring depth
 constexpr int CH = BK / 8;                       // 16-byte chunks per LDS row
 constexpr int ROWB = BK * 2;                     // bytes per LDS row
 constexpr int RPI = 64 / CH;                     // rows covered by one 1 KiB direct load
-constexpr int NI = kTile * ROWB / 1024 / 4;      // direct loads per wave, per operand, per stage
+constexpr int NI = kTile * ROWB / 1024 / WAVES;  // direct loads per wave, per operand, per stage
 constexpr int OPER_BYTES = kTile * ROWB;         // one operand tile in LDS
 constexpr int STAGE_BYTES = 2 * OPER_BYTES;
 constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
+constexpr int NS = BK / 16;                      // 16-deep MFMA steps per stage
+constexpr int LPS = KD_LPS;                      // ring loads issued per MFMA step (front-loaded)
 constexpr int SLD = kTile + 4;                   // fp32 row stride of the epilogue staging tile
 constexpr int STAGE_FLOATS = 128 * SLD;          // half a tile: 128 positions x 256 vocab
 constexpr int EPI_BYTES = (STAGE_FLOATS + 4 * kTile) * 4;
@@ -61,6 +72,7 @@ constexpr uint32_t kOOB = 0xFFFFFFF0u;           // buffer offset past any opera
 constexpr float LOG2E = 1.4426950408889634f;
 
 static_assert(BK == 32 || BK == 64, "BK");
+static_assert(LPS > 0 && LPS <= 6 && (2 * NI) % LPS == 0 && 2 * NI <= LPS * NS, "LPS");
 static_assert(STAGES >= 2, "STAGES");
 static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 
@@ -121,20 +133,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 // for outstanding loads (the LDS ring is managed with explicit vmcnt waits).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// XOR swizzle of the 16-byte chunks of LDS row r.
-__device__ __forceinline__ int swz(int r) { return CH == 8 ? (r & 7) : ((r >> 1) & 3); }
+// XOR swizzle of the 16-byte chunks of LDS row r.  gfx950 serves a
+// ds_read_b128 16 lanes at a time from 64 four-byte banks (a 256-byte
+// window); the MFMA fragment read puts 16 consecutive rows at one logical
+// chunk, and the swizzle gives those 16 rows 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int swz(int r) {
+  return CH == 8 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
+}
 
 // ------------------------------------------------------ direct LDS loads ---
 
 // Streams a 256-row, K-contiguous operand X[row][k] (leading dimension ld,
 // elements) into LDS tiles of 256 x BK.  Each wave issues NI direct loads of
-// 1 KiB; lane l of load j fills LDS row (wave*NI + j)*RPI + l/CH, physical
-// chunk l%CH, with logical chunk (l%CH) ^ swz(row).  Rows at or past row_lim
-// and columns at or past k_lim read as zero.
+// 1 KiB; lane l of load j fills LDS row r = (wave*NI + j)*RPI + l/CH,
+// physical chunk l%CH, with logical chunk (l%CH) ^ swz(r).  Rows at or past
+// row_lim and columns at or past k_lim read as zero.
 struct DLoad {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff[NI];
-  int kc;  // first k of this lane's chunk within a tile
+  int kc[NI];  // first k of this lane's chunk within a tile, per load
 
   __device__ __forceinline__ void init(const uint16_t* base, uint64_t bytes, int64_t ld, int row0,
                                        int row_lim) {
@@ -142,46 +159,53 @@ struct DLoad {
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, int(nrec), 0x00020000);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rib = lane / CH, phys = lane % CH;
-    kc = (phys ^ swz(rib)) * 8;  // block rows start at multiples of RPI: swz(row) == swz(rib)
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int row = row0 + (wave * NI + j) * RPI + rib;
-      voff[j] = row < row_lim ? uint32_t((int64_t(row) * ld + kc) * 2) : kOOB;
+      const int rt = (wave * NI + j) * RPI + rib;  // row within the tile (row0 % 256 == 0)
+      kc[j] = (phys ^ swz(rt)) * 8;
+      const int row = row0 + rt;
+      voff[j] = row < row_lim ? uint32_t((int64_t(row) * ld + kc[j]) * 2) : kOOB;
     }
   }
 
-  __device__ __forceinline__ void issue(char* stage, int k0, int k_lim) const {
+  // Load j (of NI) of the 256 x BK tile at columns [k0, k0 + BK) into stage.
+  __device__ __forceinline__ void issue_one(int j, char* stage, int k0, int k_lim) const {
     const int wave = threadIdx.x >> 6;
-    const bool kok = k0 + kc < k_lim;
+    const uint32_t off = (voff[j] != kOOB && k0 + kc[j] < k_lim) ? voff[j] + uint32_t(k0) * 2u : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * NI + j) * 1024), 16, off,
+                                             0, 0, 0);
+  }
+
+  __device__ __forceinline__ void issue(char* stage, int k0, int k_lim) const {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const uint32_t off = (kok && voff[j] != kOOB) ? voff[j] + uint32_t(k0) * 2u : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (lds_void*)(stage + (wave * NI + j) * 1024), 16, off, 0, 0, 0);
-    }
+    for (int j = 0; j < NI; ++j) issue_one(j, stage, k0, k_lim);
   }
 };
 
 // --------------------------------------------------------------- MFMA core ---
 
-// One BK-deep stage of the wave's 128 x 128 tile.  MFMA 32x32x16 operands:
+// One BK-deep stage of the wave's 128 x 64 tile.  MFMA 32x32x16 operands:
 // lane l supplies row l % 32 and the 8 consecutive k of half l / 32.
-// Fragments of the next 16-deep step load while the current step multiplies.
+// Fragments of the next 16-deep step load while the current step multiplies,
+// and the next stage's ring loads (2 * NI per wave) go out LPS per step, each
+// between two MFMAs, so loads and MFMAs of the two waves on a SIMD overlap.
 __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const char* __restrict__ sB,
-                                          f32x16 (&acc)[4][4], int wm, int wn, int lane) {
-  constexpr int NS = BK / 16;
+                                          f32x16 (&acc)[4][NJ], int wm, int wn, int lane,
+                                          const DLoad& la, const DLoad& lb, char* nst, int nk0,
+                                          int ka_lim, int kb_lim) {
+  constexpr int NR = 4 + NJ;  // fragment reads per step
   const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31);  // tile rows are r31 mod 32
   const char* pa = sA + (wm * 128 + r31) * ROWB;
-  const char* pb = sB + (wn * 128 + r31) * ROWB;
-  bf16x8 fa[2][4], fb[2][4];
+  const char* pb = sB + (wn * WT_N + r31) * ROWB;
+  bf16x8 fa[2][4], fb[2][NJ];
   {
     const int off = (hi ^ sw) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + off);
+    for (int j = 0; j < NJ; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + off);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the first step's 8 fragment reads
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // the first step's fragment reads
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int cur = s & 1;
@@ -191,67 +215,72 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
       for (int i = 0; i < 4; ++i)
         fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         fb[cur ^ 1][j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + off);
+    }
+    constexpr int NL = 2 * NI;
+    const int l0 = s * LPS;
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) {
+      const int l = l0 + q;
+      if (l < NI)
+        la.issue_one(l, nst, nk0, ka_lim);
+      else if (l < NL)
+        lb.issue_one(l - NI, nst + OPER_BYTES, nk0, kb_lim);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-    // keep the MFMA pipe fed: the next step's fragment reads go out between
-    // this step's first 8 MFMAs, so their LDS latency hides under the rest
-    if (s + 1 < NS) {
+    // 4 * NJ MFMAs; between them go the next step's fragment reads and this
+    // step's ring loads
+    const int nl = l0 < NL ? (NL - l0 < LPS ? NL - l0 : LPS) : 0;
+    const int nr = s + 1 < NS ? NR : 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    for (int q = 0; q < 4 * NJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < nl) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   }
 }
 
-// acc[i][j] (wave (wm, wn)) register r holds C[m][n] with
-//   m = wm*128 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*128 + j*32 + lane%32.
+// acc[i][j] (wave (wm, wn) = (wave / 4, wave % 4)) register r holds C[m][n] with
+//   m = wm*128 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*64 + j*32 + lane%32.
 __device__ __forceinline__ void gemm_core(const DLoad& la, const DLoad& lb, int k_begin, int k_end,
-                                          int ka_lim, int kb_lim, f32x16 (&acc)[4][4], char* smem) {
+                                          int ka_lim, int kb_lim, f32x16 (&acc)[4][NJ], char* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (k_end - k_begin + BK - 1) / BK;
   if (nk <= 0) return;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) {
-      char* st = smem + s * STAGE_BYTES;
-      la.issue(st, k_begin + s * BK, ka_lim);
-      lb.issue(st + OPER_BYTES, k_begin + s * BK, kb_lim);
-    }
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once only the newer stages' loads may be in flight
-    if (kt + STAGES - 2 < nk)
-      wait_vmcnt<(STAGES - 2) * 2 * NI>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    const int nxt = kt + STAGES - 1;
-    if (nxt < nk) {  // refill the buffer every wave finished reading last iteration
-      char* st = smem + (nxt % STAGES) * STAGE_BYTES;
-      la.issue(st, k_begin + nxt * BK, ka_lim);
-      lb.issue(st + OPER_BYTES, k_begin + nxt * BK, kb_lim);
-    }
-    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    mma_stage(st, st + OPER_BYTES, acc, wm, wn, lane);
+  for (int s = 0; s < STAGES - 1; ++s) {  // stages past the end read as zero
+    char* st = smem + s * STAGE_BYTES;
+    la.issue(st, k_begin + s * BK, ka_lim);
+    lb.issue(st + OPER_BYTES, k_begin + s * BK, kb_lim);
   }
-  lds_barrier();  // every wave is done with the ring before the epilogue reuses LDS
+  for (int kt = 0; kt < nk; ++kt) {
+    // every iteration issues one stage's loads, so once only the newer
+    // STAGES - 2 stages' loads may be in flight, stage kt has landed
+    wait_vmcnt<(STAGES - 2) * 2 * NI>();
+    lds_barrier();
+    // the next stage refills the buffer every wave finished reading last
+    // iteration; near the end it loads zeros that nothing reads
+    const int nxt = kt + STAGES - 1;
+    const int nk0 = nxt < nk ? k_begin + nxt * BK : 0x3fffffff;
+    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    mma_stage(st, st + OPER_BYTES, acc, wm, wn, lane, la, lb, smem + (nxt % STAGES) * STAGE_BYTES, nk0,
+              ka_lim, kb_lim);
+  }
+  wait_vmcnt<0>();  // the trailing zero loads land before the epilogue reuses LDS
+  lds_barrier();
 }
 
 // Row (within the 256-row tile) of accumulator register r of block i.
@@ -259,12 +288,12 @@ __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
   return wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// Writes the waves (wm, wn == half) of the tile to the staging area
-// S[position - half*128][vocab] (fp32, row stride SLD).
-__device__ __forceinline__ void stage_half(float* S, const f32x16 (&acc)[4][4], int wm, int lane) {
+// Writes a wave's part of the tile's position half (wn / 2) to the staging
+// area S[position - half*128][vocab] (fp32, row stride SLD).
+__device__ __forceinline__ void stage_half(float* S, const f32x16 (&acc)[4][NJ], int wm, int wn, int lane) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pl = j * 32 + (lane & 31);
+  for (int j = 0; j < NJ; ++j) {
+    const int pl = (wn & 1) * WT_N + j * 32 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -390,16 +419,16 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
 // ----------------------------------------------------------- logits tile ---
 
 template <int MODE>  // 0: forward epilogue, 1: backward epilogue
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(GT) void logits_kernel(LogitsArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   const int total = a.nvt * a.npt;
   const int tile = xcd_remap(blockIdx.x, total);
   const int vt = tile / a.npt, pt = tile - vt * a.npt;
   const int v0 = vt * kTile, p0 = pt * kTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
   {
     // A = W rows (vocab), B = H_c rows (positions); both D-contiguous
     DLoad la, lb;
@@ -420,7 +449,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float z = acc[i][j][r] * a.invT;
@@ -429,7 +458,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
     // per-position max and sum of exp over the tile's 256 vocab rows
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -445,13 +474,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       }
       lse_merge(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32));
       if (lane < 32) {
-        const int pl = wn * 128 + j * 32 + lane;
+        const int pl = wn * WT_N + j * 32 + lane;
         red[wm * kTile + pl] = m;
         red[(2 + wm) * kTile + pl] = s;
       }
     }
     __syncthreads();
-    {
+    if (tid < kTile) {
       float m = red[tid], s = red[2 * kTile + tid];
       lse_merge(m, s, red[kTile + tid], red[3 * kTile + tid]);
       const int prow = p0 + tid;
@@ -463,9 +492,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     if (ebeg == eend) return;
     // logits at the cached ids that fall in this tile
     for (int h = 0; h < 2; ++h) {
-      if (wn == h) stage_half(S, acc, wm, lane);
+      if ((wn >> 1) == h) stage_half(S, acc, wm, wn, lane);
       __syncthreads();
-      for (int e = ebeg + tid; e < eend; e += NT) {
+      for (int e = ebeg + tid; e < eend; e += GT) {
         const uint32_t pk = ent[e];
         const int row = int(pk >> 16);
         if ((row >> 7) == h) {
@@ -477,17 +506,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
   } else {
     const float gs = a.g_scale * (a.grad_loss != nullptr ? a.grad_loss[0] : 1.f);
-    float lse_l2[4];
+    float lse_l2[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int prow = p0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int prow = p0 + wn * WT_N + j * 32 + (lane & 31);
       lse_l2[j] = prow < a.rows ? a.lse[prow] * LOG2E : INFINITY;
     }
     // gs * softmax(z) over the full vocabulary, from the forward's lse
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float q = exp2_fast(fmaf(acc[i][j][r] * a.invT, LOG2E, -lse_l2[j]));
@@ -495,10 +524,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
           acc[i][j][r] = gs * q;
         }
     for (int h = 0; h < 2; ++h) {
-      if (wn == h) stage_half(S, acc, wm, lane);
+      if ((wn >> 1) == h) stage_half(S, acc, wm, wn, lane);
       __syncthreads();
       // minus the teacher probability at each cached id (scatter-add)
-      for (int e = ebeg + tid; e < eend; e += NT) {
+      for (int e = ebeg + tid; e < eend; e += GT) {
         const uint32_t pk = ent[e];
         const int row = int(pk >> 16);
         if ((row >> 7) == h) {
@@ -509,8 +538,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       __syncthreads();
       // G_c rows: 128 positions x 256 vocab, bf16
 #pragma unroll 4
-      for (int it = 0; it < 16; ++it) {
-        const int pl = it * 8 + (tid >> 5);
+      for (int it = 0; it < 128 * 32 / GT; ++it) {
+        const int pl = it * (GT / 32) + (tid >> 5);
         const int c8 = (tid & 31) * 8;
         const int prow = p0 + h * 128 + pl;
         if (prow < a.rows) {
@@ -526,14 +555,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       }
       // G_c^T rows: 256 vocab x 128 positions, bf16 (positions past the chunk are 0)
 #pragma unroll 4
-      for (int it = 0; it < 16; ++it) {
-        const float* col = S + (it * 8) * SLD + tid;
+      for (int it = 0; it < kTile * 16 / GT; ++it) {
+        const int vl = tid & (kTile - 1), pc = it * (GT / kTile) + tid / kTile;
+        const float* col = S + (pc * 8) * SLD + vl;
         uint4 o;
         o.x = bf16_rne(col[0]) | (bf16_rne(col[SLD]) << 16);
         o.y = bf16_rne(col[2 * SLD]) | (bf16_rne(col[3 * SLD]) << 16);
         o.z = bf16_rne(col[4 * SLD]) | (bf16_rne(col[5 * SLD]) << 16);
         o.w = bf16_rne(col[6 * SLD]) | (bf16_rne(col[7 * SLD]) << 16);
-        *reinterpret_cast<uint4*>(a.GT + int64_t(v0 + tid) * a.c_pad + p0 + h * 128 + it * 8) = o;
+        *reinterpret_cast<uint4*>(a.GT + int64_t(v0 + vl) * a.gt_ld + a.gt_col0 + p0 + h * 128 +
+                                  pc * 8) = o;
       }
       __syncthreads();
     }
@@ -625,7 +656,7 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const uint16_t* __restric
 
 // --------------------------------------------------------------- dH and dW ---
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void dh_kernel(DhArgs a) {
+__global__ __launch_bounds__(GT) void dh_kernel(DhArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[MAIN_BYTES];
   const int tiles_m = (a.rows + kTile - 1) / kTile;
   const int tiles_n = (a.D + kTile - 1) / kTile;
@@ -636,7 +667,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int k_begin = sp * a.ktiles_per_split * BK;
   int k_end = k_begin + a.ktiles_per_split * BK;
   if (k_end > a.Vp) k_end = int(a.Vp);
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
   {
     // A = G_c (positions x vocab), B = W^T (D x vocab); both vocab-contiguous
     DLoad la, lb;
@@ -645,12 +676,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     gemm_core(la, lb, k_begin, k_end, int(a.Vp), int(a.Vp), acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = tn * kTile + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int d = tn * kTile + wn * WT_N + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int prow = tm * kTile + acc_row(wm, i, r, lane);
@@ -684,32 +715,32 @@ __global__ __launch_bounds__(NT) void dh_reduce_kernel(const float* __restrict__
   reinterpret_cast<uint2*>(dH)[i] = o;
 }
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void dw_kernel(DwArgs a) {
+__global__ __launch_bounds__(GT) void dw_kernel(DwArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[MAIN_BYTES];
   const int tiles_m = int((a.V + kTile - 1) / kTile);
   const int tiles_n = (a.D + kTile - 1) / kTile;
   const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
-  const int kext = (a.rows + BK - 1) / BK * BK;  // both operands are zero past the chunk's rows
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
   {
-    // A = G_c^T (vocab x positions), B = H_c^T (D x positions); both position-contiguous
+    // A = G^T (vocab x positions), B = H^T (D x positions) of the chunk group;
+    // both position-contiguous and zero past the group's last row
     DLoad la, lb;
-    la.init(a.GT, uint64_t(a.Vp) * a.c_pad * 2, a.c_pad, tm * kTile, a.V);
-    lb.init(a.HT, uint64_t(a.D) * a.c_pad * 2, a.c_pad, tn * kTile, a.D);
-    gemm_core(la, lb, 0, kext, kext, kext, acc, smem);
+    la.init(a.GT, uint64_t(a.Vp) * a.ld * 2, a.ld, tm * kTile, a.V);
+    lb.init(a.HT, uint64_t(a.D) * a.ld * 2, a.ld, tn * kTile, a.D);
+    gemm_core(la, lb, 0, a.kext, a.kext, a.kext, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   // Read-modify-write of the fp32 dW tile, software-pipelined over the four
   // row blocks i: the old values of block i + 1 are loaded before block i is
   // stored (the blocks are disjoint rows), so two batches of 64 loads per
   // lane stay in flight instead of one.
-  float old[2][4][16];
-  auto load_block = [&](int i, float (&o)[4][16]) {
+  float old[2][NJ][16];
+  auto load_block = [&](int i, float (&o)[NJ][16]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = tn * kTile + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int d = tn * kTile + wn * WT_N + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = tm * kTile + acc_row(wm, i, r, lane);
@@ -722,8 +753,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   for (int i = 0; i < 4; ++i) {
     if (i + 1 < 4) load_block(i + 1, old[(i + 1) & 1]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = tn * kTile + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int d = tn * kTile + wn * WT_N + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = tm * kTile + acc_row(wm, i, r, lane);
@@ -776,12 +807,12 @@ hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s) {
 }
 
 hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(logits_kernel<0>, dim3(a.nvt * a.npt), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(logits_kernel<0>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(logits_kernel<1>, dim3(a.nvt * a.npt), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(logits_kernel<1>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -804,7 +835,7 @@ hipError_t launch_transpose(const uint16_t* src, int64_t ld_src, int R, int C, u
 
 hipError_t launch_dh(const DhArgs& a, hipStream_t s) {
   const int64_t tiles = ceil_div(a.rows, kTile) * ceil_div(a.D, kTile);
-  hipLaunchKernelGGL(dh_kernel, dim3(unsigned(tiles * a.split)), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(dh_kernel, dim3(unsigned(tiles * a.split)), dim3(GT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -819,7 +850,7 @@ hipError_t launch_dh_reduce(const float* part, int split, int rows, int D, int64
 
 hipError_t launch_dw(const DwArgs& a, hipStream_t s) {
   const int64_t tiles = ceil_div(a.V, kTile) * ceil_div(a.D, kTile);
-  hipLaunchKernelGGL(dw_kernel, dim3(unsigned(tiles)), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(dw_kernel, dim3(unsigned(tiles)), dim3(GT), 0, s, a);
   return hipGetLastError();
 }
 

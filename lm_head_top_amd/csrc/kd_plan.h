@@ -25,6 +25,7 @@ struct Plan {
   int64_t Vp = 0;      // V rounded up to kTile (row stride of G_c)
   int64_t npt = 0;     // position tiles per chunk
   int dh_split = 1;    // split-K factor of the dH GEMM
+  int dw_group = 1;    // chunks whose G^T and H^T feed one dW GEMM (K = dw_group * chunk)
   // workspace byte offsets
   size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0;  // shared by fwd and bwd
   size_t off_pm = 0, off_ps = 0, off_zsel = 0, off_rowkl = 0;  // forward only
@@ -39,6 +40,13 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
 
 // Split-K factor of dH = G_c W for a chunk of `c` rows and hidden size D.
 int dh_split_for(int64_t c, int64_t D);
+
+// Chunks per dW GEMM: enough that K = group * chunk reaches kDwMinK, so the
+// fp32 dW read-modify-write (8 bytes per output element) is amortised over
+// at least 2 * kDwMinK flops per element; capped at kMaxDwGroup.
+constexpr int64_t kDwMinK = 2048;
+constexpr int kMaxDwGroup = 4;
+int dw_group_for(int64_t c, int64_t N);
 
 // Pointer checks shared by the entry points.
 bool aligned(const void* p, size_t a);

@@ -55,9 +55,10 @@ def test_workspace_size_scales_with_chunk_not_N(lib):
     c = f(8192, 4096, 131072, 100, 2048)
     assert c > a
     # never O(N V): the dense fp32 grid at 32K x 131072 would be 16 GiB; the
-    # workspace is one chunk's G_c and G_c^T plus a W^T copy (O(chunk V + V D))
-    D, V, c = 4096, 131072, 1024
-    assert b <= 2 * c * V * 2 + V * D * 2 + (256 << 20)
+    # workspace is one chunk's G_c, the G^T of a group of g chunks feeding one
+    # dW GEMM (g = 2 at chunk 1024) and a W^T copy: O(chunk V + V D)
+    D, V, c, g = 4096, 131072, 1024, 2
+    assert b <= (1 + g) * c * V * 2 + V * D * 2 + (256 << 20)
 
 
 def test_workspace_size_rejects(lib):
