@@ -3,8 +3,9 @@
  * MI355X (gfx950).
  *
  * The operation is the loss described in "Distilling an LLM on One GPU:
- * Offline Top-K Logits and a Fused Chunked KL Loss" (developersdigest.tech,
- * section "The two changes") and in the scitechpulse.com news item: the student
+ * Offline Top-K Logits and a Fused Chunked KL Loss" (section "The two
+ * changes") and in "New distillation trick cuts training memory below
+ * single-GPU limit for large language models": the student
  * hidden states H[N,D] are projected through the LM head W[V,D] one chunk of
  * positions at a time, each chunk's logits are folded into a running KL loss
  * against an offline teacher cache (top-K token ids and logits per position)
@@ -79,9 +80,9 @@ size_t kd_topk_kl_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K,
                                  int64_t chunk);
 
 /*
- * Forward pass (blog section "The two changes": "processes one chunk of the
- * sequence end to end ... folds the result into the running loss, and
- * discards the chunk").
+ * Forward pass ("Distilling an LLM on One GPU", section "The two changes":
+ * each chunk of positions is projected to logits, added into the running
+ * loss and dropped before the next chunk).
  *
  *   H          bf16 [N, D]   student hidden states (read)
  *   W          bf16 [V, D]   LM-head weight, nn.Linear layout (read)
@@ -102,8 +103,8 @@ kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W,
                              void* hip_stream);
 
 /*
- * Backward pass (blog section "The two changes": "The backward pass
- * recomputes each chunk on the fly"; the projection therefore runs twice).
+ * Backward pass (same section: the backward recomputes every chunk's
+ * logits instead of keeping them, so the projection runs twice).
  *
  *   H, W, topk_idx, topk_logit, N, D, V, K, T, chunk   as in the forward
  *   lse        fp32 [N]  from the forward on the same inputs (read)

@@ -1,7 +1,8 @@
 // gfx950 kernels of the fused chunked top-K KL distillation loss.
 //
-// The method (developersdigest.tech blog, section "The two changes";
-// andresseo.expert article, section "Fused Chunked KL"): one chunk of positions
+// The method ("Distilling an LLM on One GPU", section "The two changes"; "The
+// $250GB Memory Spike That Killed Distillation Projects Is Now Optional",
+// section "Fused Chunked KL: The Loss That Never Builds the Full Grid"): one chunk of positions
 // at a time, project the hidden states to logits, fold them into the running
 // loss and drop them; the backward recomputes each chunk's logits.  Here every
 // chunk runs as

@@ -4,23 +4,24 @@ TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this module: only the tests, ``__graft_entry__.smoke()`` and the CPU
 baseline leg of ``bench.py`` use it.  It shares no code with the HIP library.
 
-What it computes (the plain dense definition; the fused method reaches the same
-objective, only in less memory -- "Neither change alters the mathematical
-objective", andresseo.expert article, section "Caching Once, Training
-Forever"):
+What it computes: the plain dense definition.  The pages state that the fused
+chunked loss changes memory use, not the objective ("The $250GB Memory Spike
+That Killed Distillation Projects Is Now Optional", section "Caching Once,
+Training Forever"), so the dense form is the reference.
 
 For positions n in [0, N), vocabulary entries v in [0, V) and cache slots k in
 [0, K), with bf16 inputs widened exactly to fp64:
 
   1. student logits  z[n, v] = (sum_d H[n, d] W[v, d]) / T
-     ("projects hidden states to logits", developersdigest.tech blog, section
-     "The two changes"; the output projection is part of the loss,
-     scitechpulse.com news item)
+     (the LM-head projection of each chunk's hidden states is part of the
+     loss: "Distilling an LLM on One GPU", section "The two changes"; "New
+     distillation trick cuts training memory below single-GPU limit")
   2. student log-normaliser  lse[n] = log sum_v exp(z[n, v])   (full vocabulary)
   3. teacher distribution renormalised over the K cached entries at temperature T
         p[n, k] = exp(t[n, k]/T - logsumexp_k t[n, .]/T)
-     (top-K cache of ids and logits: blog section "The two changes";
-     goaixin.org article, section "Detailed Chronology and Technical Evolution")
+     (top-K cache of ids and logits: "Distilling an LLM on One GPU", section
+     "The two changes"; "Breaking the Memory Barrier", section "Detailed
+     Chronology and Technical Evolution")
   4. forward KL(teacher || student) on the teacher's support
         KL_n = sum_k p[n, k] (log p[n, k] - z[n, idx[n, k]] + lse[n]),
      with 0 * log 0 := 0
