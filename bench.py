@@ -11,8 +11,11 @@ Prints one JSON line on stdout; everything else goes to stderr.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,6 +29,19 @@ PEAK_BF16_TFLOPS = 2516.6
 GEMM_KERNELS = ("logits_fwd", "logits_bwd", "dh", "dw")
 WORKLOAD_NAMES = {"tiny": "tiny", "toy": "toy_lm_head", "large_vocab": "large_vocab_head",
                   "long": "long_context", "very_long": "very_long_context"}
+# HBM traffic per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, with the
+# hash of the sources it was measured on (reported only while they are unchanged).
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("lm_head_top_amd/csrc/kd_kernels.hip", "lm_head_top_amd/csrc/kd_kernels.h",
+                  "lm_head_top_amd/csrc/kd_capi.hip", "lm_head_top_amd/csrc/kd_plan.cpp",
+                  "lm_head_top_amd/csrc/kd_plan.h")
+# demangled kernel name -> the library's kernel class name
+KERNEL_PATTERNS = (("logits_kernel<0>", "logits_fwd"), ("logits_kernel<1>", "logits_bwd"),
+                   ("dh_reduce_kernel", "dh_reduce"), ("dh_kernel", "dh"), ("dw_kernel", "dw"),
+                   ("teacher_kernel", "teacher"), ("bucket_kernel", "bucket"),
+                   ("combine_kernel", "combine"), ("finalize_kernel", "finalize"),
+                   ("transpose_kernel", "transpose"))
+COPY_KERNEL_PATTERN = "neg_kernel"   # torch.neg(fp32): reads and writes the calibration bytes once
 
 
 def log(*a):
@@ -55,6 +71,131 @@ def cpu_baseline(inp, cfg, rows):
                       f"row-blocked, block={min(cfg.chunk, rows)}); {dt:.1f} s wall"}
 
 
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _kernel_class(name: str):
+    for pat, cls in KERNEL_PATTERNS:
+        if pat in name:
+            return cls
+    return None
+
+
+def _read_counter(path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3 csv."""
+    out = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _find_csv(d: str) -> str:
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *counter_collection.csv under {d}")
+
+
+def _config_doc(cfg, seed) -> dict:
+    return {"workload": WORKLOAD_NAMES[cfg.name], "N": cfg.N, "D": cfg.D, "V": cfg.V,
+            "K": cfg.K, "chunk": cfg.chunk, "T": cfg.T, "seed": seed}
+
+
+def write_traffic(fetch_dir, write_dir, copy_mib, command, config):
+    """Turn two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) into HBM bytes per launch for each kernel class, each counter
+    scaled by what it reads for a plain fp32 copy of copy_mib MiB."""
+    fetch = _read_counter(_find_csv(fetch_dir), "FETCH_SIZE")
+    write = _read_counter(_find_csv(write_dir), "WRITE_SIZE")
+
+    def copy_reading(d, what):
+        vals = [v for n, vs in d.items() if COPY_KERNEL_PATTERN in n for v in vs]
+        if not vals:
+            raise SystemExit(f"no {COPY_KERNEL_PATTERN} dispatch in the {what} pass: "
+                             "run bench.py with --copy-calibration-mib")
+        return max(vals)
+
+    known_kib = copy_mib * 1024.0
+    f_scale = known_kib / copy_reading(fetch, "FETCH_SIZE")
+    w_scale = known_kib / copy_reading(write, "WRITE_SIZE")
+    kernels = {}
+    for d, key in ((fetch, "fetch_kib"), (write, "write_kib")):
+        for name, vals in d.items():
+            cls = _kernel_class(name)
+            if cls is None:
+                continue
+            e = kernels.setdefault(cls, {})
+            e[key + "_raw_per_launch"] = sum(vals) / len(vals)
+            e["launches_" + key.split("_")[0]] = len(vals)
+    for cls, e in kernels.items():
+        fb = e.get("fetch_kib_raw_per_launch", 0.0) * f_scale * 1024.0
+        wb = e.get("write_kib_raw_per_launch", 0.0) * w_scale * 1024.0
+        e.update(fetch_bytes_per_launch=fb, write_bytes_per_launch=wb, bytes_per_launch=fb + wb)
+    doc = {"what": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by "
+                   "its reading for a plain fp32 copy of known size",
+           "source_sha256": source_hash(), "sources": list(KERNEL_SOURCES),
+           "calibration": {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale},
+           "command": command, "config": config, "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(doc, f, indent=1, sort_keys=True)
+        f.write("\n")
+    log(f"wrote {TRAFFIC_JSON}: fetch scale {f_scale:.4f}, write scale {w_scale:.4f}")
+    for cls, e in sorted(kernels.items()):
+        log(f"  {cls:11s} {e['bytes_per_launch'] / 2**20:10.1f} MiB per launch")
+
+
+def write_stats(stats_dir, out_path, command, bench_line=None):
+    """Short text summary of a rocprofv3 --kernel-trace --stats run (its
+    kernel_stats.csv), with the bench line the same run printed."""
+    path = None
+    for root, _, files in os.walk(stats_dir):
+        for fn in files:
+            if fn.endswith("kernel_stats.csv"):
+                path = os.path.join(root, fn)
+    if path is None:
+        raise SystemExit(f"no *kernel_stats.csv under {stats_dir}")
+    with open(path, newline="") as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"# rocprofv3 kernel statistics", "", "Command (from the repository root):", "",
+             "    " + command, "",
+             "| kernel class | calls | total ms | average ms | min ms | max ms | % of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        cls = _kernel_class(name) or re.sub(r"\(.*", "", name)[:60]
+        lines.append(f"| {cls} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e6:.4f} | {float(r['MinNs']) / 1e6:.4f} | "
+                     f"{float(r['MaxNs']) / 1e6:.4f} | {float(r['Percentage']):.2f} |")
+    if bench_line:
+        lines += ["", "The bench line the same run printed:", "", "    " + bench_line.strip()]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"wrote {out_path}")
+
+
+def measured_traffic(kernel: str, config: dict):
+    """Bytes per launch of `kernel` if profiles/traffic.json was taken on the
+    current sources and the same workload, else None."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if doc.get("source_sha256") != source_hash() or doc.get("config") != config:
+        return None
+    e = doc.get("kernels", {}).get(kernel)
+    return None if e is None else e["bytes_per_launch"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -64,7 +205,34 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="positions of the CPU-oracle sample (0 skips it)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain fp32 copy of this many MiB before warmup, as the known "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --copy-calibration-mib run into profiles/traffic.json")
+    ap.add_argument("--traffic-command", default="",
+                    help="with --traffic-from / --stats-from: the profiling command, recorded")
+    ap.add_argument("--stats-from", nargs=2, metavar=("STATS_DIR", "OUT_MD"),
+                    help="no GPU run: summarise a rocprofv3 --kernel-trace --stats folder into "
+                         "OUT_MD (with the bench line from --bench-log if given)")
+    ap.add_argument("--bench-log", default=None)
     args = ap.parse_args()
+    if args.stats_from:
+        line = None
+        if args.bench_log:
+            with open(args.bench_log) as f:
+                cands = [ln for ln in f if ln.startswith("{") and '"metric"' in ln]
+            line = cands[-1] if cands else None
+        write_stats(args.stats_from[0], args.stats_from[1], args.traffic_command, line)
+        return
+    if args.traffic_from:
+        if args.copy_calibration_mib <= 0:
+            raise SystemExit("--traffic-from needs the --copy-calibration-mib the runs used")
+        from synth import get_config
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.copy_calibration_mib,
+                      args.traffic_command, _config_doc(get_config(args.config), args.seed))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the method's "
               "multi-GPU sharding is a design note, not part of this build", file=sys.stderr)
@@ -99,6 +267,13 @@ def main():
         dH, _ = kd.backward(H, W, idx, t, lse, None, cfg.T, cfg.chunk, dW=dW, workspace=ws)
         return loss, dH
 
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib * 2**18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.reset_peak_memory_stats()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -142,7 +317,8 @@ def main():
     achieved = per_launch / (dk["avg_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_launch_ms": round(dk["avg_ms"], 4),
+                "traffic": measured_traffic(dom, _config_doc(cfg, args.seed)),
+                "avg_launch_ms": round(dk["avg_ms"], 4),
                 "flops_per_launch": per_launch}
 
     base = None
@@ -158,8 +334,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; H~N(0,1), W~N(0,1/D) in bf16; Zipf(1.1) teacher ids, "
                 "sorted N(0,3) teacher logits)",
-        "config": {"workload": WORKLOAD_NAMES[cfg.name], "N": cfg.N, "D": cfg.D, "V": cfg.V,
-                   "K": cfg.K, "chunk": cfg.chunk, "T": cfg.T, "seed": args.seed},
+        "config": _config_doc(cfg, args.seed),
         "tflops": round(tflops, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "peak_hbm_gib": round(peak_gib, 3),
         "kernel_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in per_kernel.items()},

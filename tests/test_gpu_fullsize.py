@@ -4,8 +4,14 @@ The oracle cannot redo a whole problem of this size on the host in a test, so
 the checks are (a) sampled rows, which the oracle computes one by one (lse,
 KL_n and the dH row only need that row's logits), (b) properties that hold at
 any size (the loss is the mean of the per-row KL; every row of G sums to zero,
-so the columns of dW sum to zero), and (c) peak memory linear in N.
+so the columns of dW sum to zero), (c) where tests/golden holds the oracle's
+full-problem results for the workload (written by tests/golden/make_golden.py,
+which runs only the oracle), the whole loss, lse and KL_n vectors and sampled
+dW rows, and (d) peak memory linear in N.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -64,6 +70,33 @@ def test_full_size_sampled_rows(name):
     say(f"  dW column sums: worst |sum| / sum|.| = {worst:.2e}")
     assert worst <= 1e-2
     assert torch.isfinite(dW).all().item() and torch.isfinite(dH.float()).all().item()
+    _check_golden(name, loss, lse, row_kl, dW)
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _check_golden(name, loss, lse, row_kl, dW):
+    path = os.path.join(GOLDEN, f"{name}_seed0.npz")
+    if not os.path.exists(path):
+        say(f"  no oracle golden file for {name}; sampled rows and properties only")
+        return
+    import torch
+    g = np.load(path)  # plain arrays, allow_pickle stays False
+    meta = json.loads(str(g["meta"]))
+    cfg = get_config(name)
+    assert (meta["N"], meta["D"], meta["V"], meta["K"]) == (cfg.N, cfg.D, cfg.V, cfg.K)
+    e_loss = abs(loss.item() - float(g["loss"])) / abs(float(g["loss"]))
+    e_lse = np.max(np.abs(lse.double().cpu().numpy() - g["lse"]) / np.abs(g["lse"].astype(np.float64)))
+    kl_ref = g["row_kl"].astype(np.float64)
+    e_kl = np.max(np.abs(row_kl.double().cpu().numpy() - kl_ref) / np.abs(kl_ref))
+    rows = torch.from_numpy(g["dw_rows"]).to(dW.device)
+    got = dW.index_select(0, rows).double().cpu().numpy()
+    e_dw = max(rel(got[i], g["dw"][i]) for i in range(got.shape[0]))
+    say(f"  golden: loss rel {e_loss:.2e}, all-rows lse rel {e_lse:.2e}, row_kl rel {e_kl:.2e}, "
+        f"dW rows {g['dw_rows'].tolist()} worst rel L2 {e_dw:.2e}")
+    assert e_loss <= LOSS_RTOL and e_lse <= LOSS_RTOL and e_kl <= LOSS_RTOL
+    assert e_dw <= GRAD_RTOL
 
 
 def test_peak_memory_linear_in_N():
