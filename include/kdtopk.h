@@ -110,7 +110,11 @@ kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W,
  *   lse        fp32 [N]  from the forward on the same inputs (read)
  *   grad_loss  fp32 [1]  device scalar dLoss_out/dloss, or NULL for 1
  *   dH         bf16 [N, D]  overwritten with G W
- *   dW         fp32 [V, D]  accumulated: dW += G^T H (zero it for a fresh gradient)
+ *   dW         fp32 [V, D]  accumulated: dW += G^T H (zero it for a fresh gradient).
+ *              Device memory from hipMalloc: the accumulation uses fp32
+ *              atomic adds in L2, one per element per dW GEMM, so the result
+ *              equals a plain read-modify-write and is deterministic.  Calls
+ *              that accumulate into the same dW must be ordered (one stream).
  *   workspace  as in the forward
  */
 kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W,
@@ -131,6 +135,13 @@ kd_status kd_topk_kl_validate(const int32_t* topk_idx, int64_t N, int32_t K,
 
 /* Static, human-readable name of a status code. */
 const char* kd_status_string(kd_status s);
+
+/*
+ * Name of the HIP error (hipGetErrorName) behind the most recent KD_ERR_HIP
+ * returned on the calling thread, or "" if there was none.  Static storage;
+ * the caller does not free it.
+ */
+const char* kd_last_hip_error(void);
 
 /*
  * Measurement aids.  kd_profile_enable(mask) makes every later launch of each

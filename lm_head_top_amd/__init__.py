@@ -31,9 +31,11 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem size",
 
 
 class KDError(RuntimeError):
-    def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {_STATUS.get(status, 'unknown')} (status {status})")
+    def __init__(self, status: int, what: str, hip_error: str = ""):
+        detail = f", {hip_error}" if hip_error else ""
+        super().__init__(f"{what}: {_STATUS.get(status, 'unknown')} (status {status}{detail})")
         self.status = status
+        self.hip_error = hip_error
 
 
 def lib_path() -> str:
@@ -50,6 +52,11 @@ def load_library():
         raise ImportError(
             f"{path} is missing: build it with `python -m lm_head_top_amd.build` "
             "(or __graft_entry__.build()); there is no non-HIP fallback")
+    # The library finds libamdhip64 by soname.  Loading torch first makes it
+    # bind to the HIP runtime torch has already loaded, so the device pointers
+    # and streams torch hands over belong to the same runtime (loaded the other
+    # way round, the process would hold two HIP runtimes).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     c_i64, c_i32, c_f, c_vp, c_sz = (ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_size_t)
@@ -65,6 +72,8 @@ def load_library():
     lib.kd_topk_kl_validate.restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
+    lib.kd_last_hip_error.argtypes = []
+    lib.kd_last_hip_error.restype = ctypes.c_char_p
     lib.kd_profile_enable.argtypes = [ctypes.c_uint32]
     lib.kd_profile_enable.restype = ctypes.c_int
     lib.kd_profile_read.argtypes = [c_i32, ctypes.POINTER(ctypes.c_double),
@@ -76,7 +85,8 @@ def load_library():
 
 def _check(status: int, what: str):
     if status != 0:
-        raise KDError(status, what)
+        hip = _lib.kd_last_hip_error().decode() if status == 4 and _lib is not None else ""
+        raise KDError(status, what, hip)
 
 
 def workspace_size(N: int, D: int, V: int, K: int, chunk: int) -> int:

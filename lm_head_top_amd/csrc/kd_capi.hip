@@ -37,10 +37,18 @@ hipError_t timed(int id, hipStream_t s, F&& launch) {
   return e;
 }
 
-#define KD_LAUNCH(id, stream, call)                              \
-  do {                                                           \
-    if (timed((id), (stream), [&] { return (call); }) != hipSuccess) \
-      return KD_ERR_HIP;                                         \
+// The HIP error behind the calling thread's most recent KD_ERR_HIP.
+thread_local hipError_t t_last_hip = hipSuccess;
+
+kd_status hip_failed(hipError_t e) {
+  t_last_hip = e;
+  return KD_ERR_HIP;
+}
+
+#define KD_LAUNCH(id, stream, call)                                    \
+  do {                                                                 \
+    const hipError_t kd_e_ = timed((id), (stream), [&] { return (call); }); \
+    if (kd_e_ != hipSuccess) return hip_failed(kd_e_);                 \
   } while (0)
 
 bool bad_ptr(const void* p, size_t align) { return p == nullptr || !kd::aligned(p, align); }
@@ -63,6 +71,10 @@ const char* kd_status_string(kd_status s) {
       return "HIP launch failed";
   }
   return "unknown status";
+}
+
+const char* kd_last_hip_error(void) {
+  return t_last_hip == hipSuccess ? "" : hipGetErrorName(t_last_hip);
 }
 
 size_t kd_topk_kl_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int64_t chunk) {
@@ -230,7 +242,8 @@ kd_status kd_topk_kl_validate(const int32_t* topk_idx, int64_t N, int32_t K, int
   if (N < 0 || K <= 0 || V <= 0 || K > KD_MAX_K) return KD_ERR_INVALID_ARG;
   if (N > 0 && bad_ptr(topk_idx, 4)) return KD_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (kd::launch_validate(topk_idx, N, K, V, d_flags, s) != hipSuccess) return KD_ERR_HIP;
+  const hipError_t e = kd::launch_validate(topk_idx, N, K, V, d_flags, s);
+  if (e != hipSuccess) return hip_failed(e);
   return KD_OK;
 }
 

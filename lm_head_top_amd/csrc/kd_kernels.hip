@@ -19,17 +19,18 @@
 //   combine   forward: merge the vocab-tile partials into lse and KL per row;
 //   dh / dw   dH_c = G_c W (split over V, fp32 partials) and dW += G_c^T H_c.
 //
-// GEMM core: 512 threads (2 x 4 waves of 64, two waves per SIMD), a 256 x 256
-// output tile with a 128 x 64 tile per wave held as 4 x 2 MFMA 32x32 fp32
-// accumulators.  A wave that stalls issuing a load leaves its SIMD to the
-// other wave's MFMAs.  Both
-// operands are K-contiguous in memory (the backward keeps W^T, H_c^T and
-// G_c^T copies so that every GEMM reads K-contiguous rows).  Tiles of BK
-// columns stream from HBM straight into LDS with buffer_load_dwordx4 ... lds
-// (no register staging; out-of-range rows and columns read as zero), through
-// a ring of STAGES buffers.  Inside a row of the LDS tile the 16-byte chunks
-// are XOR-swizzled by row so the MFMA fragment reads (ds_read_b128, lanes on
-// 32 consecutive rows at one k offset) hit distinct banks.
+// GEMM core: a 256 x 256 output tile per workgroup, split over waves 2 (M) x
+// WAVES/2 (N); each wave holds its (128 x 256/(WAVES/2)) part as 32x32 fp32
+// MFMA accumulators.  Both operands are K-contiguous in memory (the backward
+// keeps W^T, H_c^T and G_c^T copies so that every GEMM reads K-contiguous
+// rows).  Tiles of BK columns stream from HBM straight into LDS with
+// buffer_load_dwordx4 ... lds (no register staging; out-of-range rows and
+// columns read as zero), through a ring of STAGES buffers.  Inside a row of
+// the LDS tile the 16-byte chunks are XOR-swizzled by row so the MFMA
+// fragment reads (ds_read_b128, lanes on 32 consecutive rows at one k
+// offset) hit distinct banks.  A compute unit accepts one 1 KiB direct load
+// about every 20 cycles for all its waves together, so the loads are spread
+// between the MFMAs rather than issued in a burst.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -42,18 +43,34 @@
 #ifndef KD_STAGES
 #define KD_STAGES 2
 #endif
+#ifndef KD_WAVES
+#define KD_WAVES 8
+#endif
 #ifndef KD_LPS
-#define KD_LPS 4
+#define KD_LPS (KD_WAVES == 8 ? 4 : 4)
+#endif
+#ifndef KD_VSPREAD
+#define KD_VSPREAD 0
+#endif
+#ifndef KD_LOAD_AUX
+#define KD_LOAD_AUX 0
+#endif
+#ifndef KD_DW_BAND
+#define KD_DW_BAND 0
 #endif
 
 namespace kd {
 namespace {
 
 constexpr int NT = 256;                          // threads of the small kernels
-constexpr int GT = 512;                          // threads per GEMM workgroup: 8 waves, 2 per SIMD
-constexpr int WAVES = GT / 64;
-constexpr int WT_N = 64;                         // wave tile: 128 (M) x 64 (N), waves 2 (M) x 4 (N)
-constexpr int NJ = WT_N / 32;                    // 32-wide MFMA blocks per wave along N
+constexpr int WAVES = KD_WAVES;                  // 8: two waves per SIMD; 4: one
+constexpr int GT = WAVES * 64;                   // threads per GEMM workgroup
+constexpr int WAVES_M = 2;
+constexpr int WAVES_N = WAVES / WAVES_M;
+constexpr int WT_M = kTile / WAVES_M;            // wave tile rows (128)
+constexpr int WT_N = kTile / WAVES_N;            // wave tile columns (64 or 128)
+constexpr int MI = WT_M / 32;                    // 32-row MFMA blocks per wave
+constexpr int NJ = WT_N / 32;                    // 32-column MFMA blocks per wave
 constexpr int BK = KD_BK;                        // K columns per pipeline stage
 constexpr int STAGES = KD_STAGES;                // LDS ring depth
 constexpr int CH = BK / 8;                       // 16-byte chunks per LDS row
@@ -73,9 +90,14 @@ constexpr uint32_t kOOB = 0xFFFFFFF0u;           // buffer offset past any opera
 constexpr float LOG2E = 1.4426950408889634f;
 
 static_assert(BK == 32 || BK == 64, "BK");
-static_assert(LPS > 0 && LPS <= 6 && (2 * NI) % LPS == 0 && 2 * NI <= LPS * NS, "LPS");
+static_assert(WAVES == 4 || WAVES == 8, "WAVES");
+static_assert(LPS > 0 && LPS <= MI * NJ && (2 * NI) % LPS == 0 && 2 * NI <= LPS * NS, "LPS");
 static_assert(STAGES >= 2, "STAGES");
 static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+
+// GEMM kernels: one workgroup per compute unit; with 4 waves each wave may use
+// the whole register file of its SIMD (accumulators in AGPRs).
+#define KD_GEMM_KERNEL __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
@@ -174,7 +196,7 @@ struct DLoad {
     const int wave = threadIdx.x >> 6;
     const uint32_t off = (voff[j] != kOOB && k0 + kc[j] < k_lim) ? voff[j] + uint32_t(k0) * 2u : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * NI + j) * 1024), 16, off,
-                                             0, 0, 0);
+                                             0, 0, KD_LOAD_AUX);
   }
 
   __device__ __forceinline__ void issue(char* stage, int k0, int k_lim) const {
@@ -185,24 +207,25 @@ struct DLoad {
 
 // --------------------------------------------------------------- MFMA core ---
 
-// One BK-deep stage of the wave's 128 x 64 tile.  MFMA 32x32x16 operands:
+// One BK-deep stage of the wave's WT_M x WT_N tile.  MFMA 32x32x16 operands:
 // lane l supplies row l % 32 and the 8 consecutive k of half l / 32.
 // Fragments of the next 16-deep step load while the current step multiplies,
 // and the next stage's ring loads (2 * NI per wave) go out LPS per step, each
-// between two MFMAs, so loads and MFMAs of the two waves on a SIMD overlap.
+// between two MFMAs.
 __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const char* __restrict__ sB,
-                                          f32x16 (&acc)[4][NJ], int wm, int wn, int lane,
+                                          f32x16 (&acc)[MI][NJ], int wm, int wn, int lane,
                                           const DLoad& la, const DLoad& lb, char* nst, int nk0,
                                           int ka_lim, int kb_lim) {
-  constexpr int NR = 4 + NJ;  // fragment reads per step
+  constexpr int NR = MI + NJ;  // fragment reads per step
+  constexpr int NQ = MI * NJ;  // MFMAs per step
   const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31);  // tile rows are r31 mod 32
-  const char* pa = sA + (wm * 128 + r31) * ROWB;
+  const char* pa = sA + (wm * WT_M + r31) * ROWB;
   const char* pb = sB + (wn * WT_N + r31) * ROWB;
-  bf16x8 fa[2][4], fb[2][NJ];
+  bf16x8 fa[2][MI], fb[2][NJ];
   {
     const int off = (hi ^ sw) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
+    for (int i = 0; i < MI; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + off);
   }
@@ -213,7 +236,7 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
     if (s + 1 < NS) {
       const int off = ((2 * (s + 1) + hi) ^ sw) * 16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
         fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
@@ -230,31 +253,32 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
         lb.issue_one(l - NI, nst + OPER_BYTES, nk0, kb_lim);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-    // 4 * NJ MFMAs; between them go the next step's fragment reads and this
-    // step's ring loads
+    // NQ MFMAs; between them go the next step's fragment reads and this
+    // step's ring loads (spread evenly, or one after each of the first MFMAs)
     const int nl = l0 < NL ? (NL - l0 < LPS ? NL - l0 : LPS) : 0;
     const int nr = s + 1 < NS ? NR : 0;
 #pragma unroll
-    for (int q = 0; q < 4 * NJ; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (q < nl) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (KD_VSPREAD ? (nl > 0 && q % (NQ / LPS) == 0 && q / (NQ / LPS) < nl) : (q < nl))
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   }
 }
 
-// acc[i][j] (wave (wm, wn) = (wave / 4, wave % 4)) register r holds C[m][n] with
-//   m = wm*128 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*64 + j*32 + lane%32.
+// acc[i][j] (wave (wm, wn) = (wave / WAVES_N, wave % WAVES_N)) register r holds C[m][n] with
+//   m = wm*WT_M + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*WT_N + j*32 + lane%32.
 __device__ __forceinline__ void gemm_core(const DLoad& la, const DLoad& lb, int k_begin, int k_end,
-                                          int ka_lim, int kb_lim, f32x16 (&acc)[4][NJ], char* smem) {
+                                          int ka_lim, int kb_lim, f32x16 (&acc)[MI][NJ], char* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -286,20 +310,26 @@ __device__ __forceinline__ void gemm_core(const DLoad& la, const DLoad& lb, int 
 
 // Row (within the 256-row tile) of accumulator register r of block i.
 __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  return wm * WT_M + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// Writes a wave's part of the tile's position half (wn / 2) to the staging
-// area S[position - half*128][vocab] (fp32, row stride SLD).
-__device__ __forceinline__ void stage_half(float* S, const f32x16 (&acc)[4][NJ], int wm, int wn, int lane) {
+// Column (within the tile) of the accumulators of block j.
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * WT_N + j * 32 + (lane & 31); }
+
+// Writes the wave's columns that fall in half h (columns h*128 .. h*128+127)
+// to the staging area S[column - h*128][row] (fp32, row stride SLD).
+__device__ __forceinline__ void stage_half(float* S, const f32x16 (&acc)[MI][NJ], int wm, int wn, int lane,
+                                           int h) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int pl = (wn & 1) * WT_N + j * 32 + (lane & 31);
+    const int col = acc_col(wn, j, lane);
+    if ((wn * WT_N + j * 32) >> 7 != h) continue;  // uniform per wave
+    const int pl = col & 127;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int vl = wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
+        const int vl = wm * WT_M + i * 32 + 8 * g + 4 * (lane >> 5);
         *reinterpret_cast<float4*>(S + pl * SLD + vl) =
             make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
       }
@@ -420,16 +450,16 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
 // ----------------------------------------------------------- logits tile ---
 
 template <int MODE>  // 0: forward epilogue, 1: backward epilogue
-__global__ __launch_bounds__(GT) void logits_kernel(LogitsArgs a) {
+KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   const int total = a.nvt * a.npt;
   const int tile = xcd_remap(blockIdx.x, total);
   const int vt = tile / a.npt, pt = tile - vt * a.npt;
   const int v0 = vt * kTile, p0 = pt * kTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  f32x16 acc[4][NJ];
+  f32x16 acc[MI][NJ];
   {
     // A = W rows (vocab), B = H_c rows (positions); both D-contiguous
     DLoad la, lb;
@@ -448,7 +478,7 @@ __global__ __launch_bounds__(GT) void logits_kernel(LogitsArgs a) {
   if (MODE == 0) {
     // z = acc / T; vocab rows past V do not exist
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -462,20 +492,20 @@ __global__ __launch_bounds__(GT) void logits_kernel(LogitsArgs a) {
     for (int j = 0; j < NJ; ++j) {
       float m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
       float s = 0.f;
       if (m != -INFINITY) {
         const float mb = m * LOG2E;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s += exp2_fast(fmaf(acc[i][j][r], LOG2E, -mb));
       }
       lse_merge(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32));
       if (lane < 32) {
-        const int pl = wn * WT_N + j * 32 + lane;
+        const int pl = acc_col(wn, j, lane);
         red[wm * kTile + pl] = m;
         red[(2 + wm) * kTile + pl] = s;
       }
@@ -493,7 +523,7 @@ __global__ __launch_bounds__(GT) void logits_kernel(LogitsArgs a) {
     if (ebeg == eend) return;
     // logits at the cached ids that fall in this tile
     for (int h = 0; h < 2; ++h) {
-      if ((wn >> 1) == h) stage_half(S, acc, wm, wn, lane);
+      stage_half(S, acc, wm, wn, lane, h);
       __syncthreads();
       for (int e = ebeg + tid; e < eend; e += GT) {
         const uint32_t pk = ent[e];
@@ -510,12 +540,12 @@ __global__ __launch_bounds__(GT) void logits_kernel(LogitsArgs a) {
     float lse_l2[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int prow = p0 + wn * WT_N + j * 32 + (lane & 31);
+      const int prow = p0 + acc_col(wn, j, lane);
       lse_l2[j] = prow < a.rows ? a.lse[prow] * LOG2E : INFINITY;
     }
     // gs * softmax(z) over the full vocabulary, from the forward's lse
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -525,7 +555,7 @@ __global__ __launch_bounds__(GT) void logits_kernel(LogitsArgs a) {
           acc[i][j][r] = gs * q;
         }
     for (int h = 0; h < 2; ++h) {
-      if ((wn >> 1) == h) stage_half(S, acc, wm, wn, lane);
+      stage_half(S, acc, wm, wn, lane, h);
       __syncthreads();
       // minus the teacher probability at each cached id (scatter-add)
       for (int e = ebeg + tid; e < eend; e += GT) {
@@ -657,7 +687,7 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const uint16_t* __restric
 
 // --------------------------------------------------------------- dH and dW ---
 
-__global__ __launch_bounds__(GT) void dh_kernel(DhArgs a) {
+KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[MAIN_BYTES];
   const int tiles_m = (a.rows + kTile - 1) / kTile;
   const int tiles_n = (a.D + kTile - 1) / kTile;
@@ -668,7 +698,7 @@ __global__ __launch_bounds__(GT) void dh_kernel(DhArgs a) {
   const int k_begin = sp * a.ktiles_per_split * BK;
   int k_end = k_begin + a.ktiles_per_split * BK;
   if (k_end > a.Vp) k_end = int(a.Vp);
-  f32x16 acc[4][NJ];
+  f32x16 acc[MI][NJ];
   {
     // A = G_c (positions x vocab), B = W^T (D x vocab); both vocab-contiguous
     DLoad la, lb;
@@ -677,12 +707,12 @@ __global__ __launch_bounds__(GT) void dh_kernel(DhArgs a) {
     gemm_core(la, lb, k_begin, k_end, int(a.Vp), int(a.Vp), acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int d = tn * kTile + wn * WT_N + j * 32 + (lane & 31);
+      const int d = tn * kTile + acc_col(wn, j, lane);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int prow = tm * kTile + acc_row(wm, i, r, lane);
@@ -716,13 +746,29 @@ __global__ __launch_bounds__(NT) void dh_reduce_kernel(const float* __restrict__
   reinterpret_cast<uint2*>(dH)[i] = o;
 }
 
-__global__ __launch_bounds__(GT) void dw_kernel(DwArgs a) {
+KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[MAIN_BYTES];
   const int tiles_m = int((a.V + kTile - 1) / kTile);
   const int tiles_n = (a.D + kTile - 1) / kTile;
   const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+#if KD_DW_BAND
+  // bands of KD_DW_BAND output-column tiles; inside a band, vocab-tile major
+  constexpr int GN = KD_DW_BAND;
+  const int nb = tiles_n / GN;
+  int tm, tn;
+  if (tile < nb * GN * tiles_m) {
+    const int band = tile / (GN * tiles_m), r = tile - band * GN * tiles_m;
+    tm = r / GN;
+    tn = band * GN + (r - tm * GN);
+  } else {
+    const int w = tiles_n - nb * GN, r = tile - nb * GN * tiles_m;
+    tm = r / w;
+    tn = nb * GN + (r - tm * w);
+  }
+#else
   const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
-  f32x16 acc[4][NJ];
+#endif
+  f32x16 acc[MI][NJ];
   {
     // A = G^T (vocab x positions), B = H^T (D x positions) of the chunk group;
     // both position-contiguous and zero past the group's last row
@@ -732,37 +778,22 @@ __global__ __launch_bounds__(GT) void dw_kernel(DwArgs a) {
     gemm_core(la, lb, 0, a.kext, a.kext, a.kext, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  // Read-modify-write of the fp32 dW tile, software-pipelined over the four
-  // row blocks i: the old values of block i + 1 are loaded before block i is
-  // stored (the blocks are disjoint rows), so two batches of 64 loads per
-  // lane stay in flight instead of one.
-  float old[2][NJ][16];
-  auto load_block = [&](int i, float (&o)[NJ][16]) {
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  // dW += tile with one fp32 atomic add per element (no value returned): the
+  // read-modify-write happens in L2, so the workgroup does not wait for the
+  // old values.  Each element gets exactly one add per launch, so the result
+  // equals a plain read-modify-write and does not depend on timing.
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int d = tn * kTile + wn * WT_N + j * 32 + (lane & 31);
+      const int d = tn * kTile + acc_col(wn, j, lane);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = tm * kTile + acc_row(wm, i, r, lane);
-        o[j][r] = (v < a.V && d < a.D) ? a.dW[int64_t(v) * a.D + d] : 0.f;
+        if (v < a.V && d < a.D) unsafeAtomicAdd(a.dW + int64_t(v) * a.D + d, acc[i][j][r]);
       }
     }
-  };
-  load_block(0, old[0]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i + 1 < 4) load_block(i + 1, old[(i + 1) & 1]);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int d = tn * kTile + wn * WT_N + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = tm * kTile + acc_row(wm, i, r, lane);
-        if (v < a.V && d < a.D) a.dW[int64_t(v) * a.D + d] = old[i & 1][j][r] + acc[i][j][r];
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------- utility ---

@@ -44,7 +44,10 @@ int dh_split_for(int64_t c, int64_t D);
 // Chunks per dW GEMM: enough that K = group * chunk reaches kDwMinK, so the
 // fp32 dW read-modify-write (8 bytes per output element) is amortised over
 // at least 2 * kDwMinK flops per element; capped at kMaxDwGroup.
-constexpr int64_t kDwMinK = 2048;
+#ifndef KD_DW_MIN_K
+#define KD_DW_MIN_K 4096
+#endif
+constexpr int64_t kDwMinK = KD_DW_MIN_K;
 constexpr int kMaxDwGroup = 4;
 int dw_group_for(int64_t c, int64_t N);
 

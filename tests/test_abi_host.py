@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("kd_topk_kl_forward", "kd_topk_kl_backward", "kd_topk_kl_workspace_size",
-                 "kd_topk_kl_validate", "kd_status_string"):
+                 "kd_topk_kl_validate", "kd_status_string", "kd_last_hip_error"):
         assert want in names
 
 
@@ -46,6 +46,13 @@ def test_status_strings(lib):
     assert lib.kd_status_string(99) == b"unknown status"
 
 
+def test_last_hip_error_is_empty_without_a_failed_launch(lib):
+    # argument errors are not HIP errors
+    assert lib.kd_topk_kl_forward(None, None, None, None, 1, 8, 8, 1, 1.0, 1, None, None, None,
+                                  None, 0, None) == KD_ERR_INVALID_ARG
+    assert lib.kd_last_hip_error() == b""
+
+
 def test_workspace_size_scales_with_chunk_not_N(lib):
     f = kd.workspace_size
     a = f(8192, 4096, 131072, 100, 1024)
@@ -56,8 +63,8 @@ def test_workspace_size_scales_with_chunk_not_N(lib):
     assert c > a
     # never O(N V): the dense fp32 grid at 32K x 131072 would be 16 GiB; the
     # workspace is one chunk's G_c, the G^T of a group of g chunks feeding one
-    # dW GEMM (g = 2 at chunk 1024) and a W^T copy: O(chunk V + V D)
-    D, V, c, g = 4096, 131072, 1024, 2
+    # dW GEMM (g = 4 at chunk 1024) and a W^T copy: O(chunk V + V D)
+    D, V, c, g = 4096, 131072, 1024, 4
     assert b <= (1 + g) * c * V * 2 + V * D * 2 + (256 << 20)
 
 
@@ -169,3 +176,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         mod.load_library()
     monkeypatch.undo()
     importlib.reload(kd)
+
+
+def test_one_hip_runtime_in_the_process():
+    """Loading the library binds it to the HIP runtime torch uses, whatever was
+    imported first (checked in a fresh interpreter)."""
+    import subprocess
+    import sys
+    code = ("import lm_head_top_amd as kd; kd.load_library(); "
+            "m = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))")
+    if not os.path.exists(kd.lib_path()):
+        pytest.skip("libkdtopk.so not built")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"
