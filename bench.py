@@ -196,6 +196,132 @@ def measured_traffic(kernel: str, config: dict):
     return None if e is None else e["bytes_per_launch"]
 
 
+def _gpu_inputs(torch, N, D, V, K, seed, dev):
+    """Seeded device-side random inputs of the workload's shapes (for the memory
+    sweep, whose largest sizes are slow to draw on the host)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    H = torch.randn((N, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    idx = torch.randint(0, V, (N, K), generator=g, device=dev, dtype=torch.int32)
+    t = torch.sort(torch.randn((N, K), generator=g, device=dev) * 3 ** 0.5, dim=1,
+                   descending=True).values
+    return H, idx, t
+
+
+def memory_sweep(args):
+    """Peak device memory and time of one forward + backward for growing N at
+    D = 4096, V = 131072, K = 100, chunk = 2048: the fused loss keeps memory
+    linear in N (no N x V term).  Prints one JSON line with the fit."""
+    import numpy as np
+    import torch
+    import lm_head_top_amd as kd
+    kd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    D, V, K, chunk, T = 4096, 131072, 100, 2048, 1.0
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    W = (torch.randn((V, D), generator=g, device=dev) * D ** -0.5).to(torch.bfloat16)
+    dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
+    points = []
+    for N in args.sweep_n:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        H, idx, t = _gpu_inputs(torch, N, D, V, K, args.seed + N, dev)
+        loss, lse = kd.forward(H, W, idx, t, T, chunk)  # warm-up call
+        kd.backward(H, W, idx, t, lse, None, T, chunk, dW=dW)
+        del loss, lse
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        loss, lse = kd.forward(H, W, idx, t, T, chunk)
+        dH, _ = kd.backward(H, W, idx, t, lse, None, T, chunk, dW=dW)
+        e1.record()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated()
+        ms = e0.elapsed_time(e1)
+        points.append({"N": N, "peak_gib": round(peak / 2**30, 4), "ms": round(ms, 3),
+                       "tokens_per_s": round(N / (ms * 1e-3), 1)})
+        log(f"N={N}: peak {peak / 2**30:.3f} GiB, {ms:.2f} ms, loss {loss.item():.5f}")
+        del H, idx, t, loss, lse, dH
+    x = np.array([p["N"] for p in points], dtype=np.float64)
+    y = np.array([p["peak_gib"] for p in points], dtype=np.float64) * 2**30
+    slope, icpt = np.polyfit(x, y, 1)
+    resid = float(np.max(np.abs(y - (slope * x + icpt)) / y))
+    line = {"mode": "memory_sweep", "D": D, "V": V, "K": K, "chunk": chunk,
+            "points": points, "slope_kib_per_token": round(slope / 1024, 3),
+            "intercept_gib": round(icpt / 2**30, 3), "max_rel_residual": round(resid, 5),
+            "note": "peak = torch.cuda.max_memory_allocated over one forward + backward, "
+                    "including W, dW, H, cache, lse, dH and the workspace"}
+    print(json.dumps(line), flush=True)
+
+
+def dense_reference(args):
+    """The dense loss in plain PyTorch eager autograd (full [N, V] logits in fp32)
+    beside the fused loss on the same inputs: peak memory and time of one
+    forward + backward.  A measurement aid; the library does not use it."""
+    import numpy as np
+    import torch
+    import lm_head_top_amd as kd
+    from synth import get_config, make_inputs
+    kd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    inp = make_inputs(cfg, args.seed)
+    H = torch.from_numpy(inp["H"].view(np.int16)).view(torch.bfloat16).to(dev)
+    W = torch.from_numpy(inp["W"].view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(inp["idx"]).to(dev)
+    t = torch.from_numpy(inp["t"]).to(dev)
+    N, T = cfg.N, cfg.T
+
+    def dense_step():
+        Hg = H.detach().requires_grad_(True)
+        Wt = W.detach().t().contiguous().requires_grad_(True)  # [D, V]; plain 2-D products only
+        z = (Hg @ Wt).float() / T
+        logq = torch.log_softmax(z, dim=-1)
+        lq = logq.gather(1, idx.long())
+        logp = torch.log_softmax(t / T, dim=-1)
+        loss = (logp.exp() * (logp - lq)).sum() / N
+        loss.backward()
+        return loss.detach(), Hg.grad, Wt.grad
+
+    def fused_step():
+        loss, lse = kd.forward(H, W, idx, t, T, cfg.chunk)
+        dH, dW = kd.backward(H, W, idx, t, lse, None, T, cfg.chunk)
+        return loss, dH, dW
+
+    out = {}
+    for name, fn in (("fused", fused_step), ("dense", dense_step)):
+        fn()  # warm-up (library and allocator)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        times = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            res = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        peak = torch.cuda.max_memory_allocated()
+        out[name] = {"ms_median": round(sorted(times)[1], 3), "peak_gib": round(peak / 2**30, 3),
+                     "peak_above_inputs_gib": round((peak - base) / 2**30, 3),
+                     "loss": float(res[0].item())}
+        log(f"{name}: {out[name]}")
+        del res
+    rel = abs(out["fused"]["loss"] - out["dense"]["loss"]) / abs(out["dense"]["loss"])
+    line = {"mode": "dense_reference", "config": _config_doc(cfg, args.seed), **out,
+            "loss_rel_diff": rel,
+            "dense_grid_fp32_gib": round(N * cfg.V * 4 / 2**30, 3),
+            "speedup_fused_over_dense": round(out["dense"]["ms_median"] / out["fused"]["ms_median"], 3),
+            "memory_ratio_dense_over_fused": round(out["dense"]["peak_gib"] / out["fused"]["peak_gib"], 3)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,7 +343,20 @@ def main():
                     help="no GPU run: summarise a rocprofv3 --kernel-trace --stats folder into "
                          "OUT_MD (with the bench line from --bench-log if given)")
     ap.add_argument("--bench-log", default=None)
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="peak memory and time of one forward + backward for N in --sweep-n "
+                         "(D=4096, V=131072, K=100, chunk=2048); prints the linear fit")
+    ap.add_argument("--sweep-n", type=int, nargs="+",
+                    default=[8192, 16384, 32768, 65536, 131072, 262144])
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="plain PyTorch dense loss beside the fused one on --config "
+                         "(peak memory, time)")
     args = ap.parse_args()
+    if args.memory_sweep or args.dense_reference:
+        if args.gpus != 1:
+            sys.exit(2)
+        (memory_sweep if args.memory_sweep else dense_reference)(args)
+        return
     if args.stats_from:
         line = None
         if args.bench_log:
@@ -283,17 +422,27 @@ def main():
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    # per step: start, forward done, backward done
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        loss, dH = step()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        loss, lse = kd.forward(H, W, idx, t, cfg.T, cfg.chunk, workspace=ws)
+        evs[i][1].record(stream)
+        dH, _ = kd.backward(H, W, idx, t, lse, None, cfg.T, cfg.chunk, dW=dW, workspace=ws)
+        evs[i][2].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     kd.profile_enable(None)
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
+    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    med = lambda v: v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
     peak_gib = torch.cuda.max_memory_allocated() / 2**30
     per_kernel = {}
     for k in GEMM_KERNELS:
@@ -337,6 +486,8 @@ def main():
         "config": _config_doc(cfg, args.seed),
         "tflops": round(tflops, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "peak_hbm_gib": round(peak_gib, 3),
+        "median_ms": {"step": round(med(step_ms), 4), "forward": round(med(fwd_ms), 4),
+                      "backward": round(med(bwd_ms), 4)},
         "kernel_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in per_kernel.items()},
         "roofline": roofline, "cpu_baseline": base,
     }
