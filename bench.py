@@ -39,8 +39,7 @@ KERNEL_SOURCES = ("lm_head_top_amd/csrc/kd_kernels.hip", "lm_head_top_amd/csrc/k
 KERNEL_PATTERNS = (("logits_kernel<0>", "logits_fwd"), ("logits_kernel<1>", "logits_bwd"),
                    ("dh_reduce_kernel", "dh_reduce"), ("dh_kernel", "dh"), ("dw_kernel", "dw"),
                    ("teacher_kernel", "teacher"), ("bucket_kernel", "bucket"),
-                   ("combine_kernel", "combine"), ("finalize_kernel", "finalize"),
-                   ("transpose_kernel", "transpose"))
+                   ("combine_kernel", "combine"), ("finalize_kernel", "finalize"))
 COPY_KERNEL_PATTERN = "neg_kernel"   # torch.neg(fp32): reads and writes the calibration bytes once
 
 

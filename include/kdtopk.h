@@ -161,8 +161,7 @@ enum {
   KD_KERNEL_DH_REDUCE = 6,  /* sum of the dH split partials */
   KD_KERNEL_DW = 7,         /* dW += G^T H */
   KD_KERNEL_BUCKET = 8,     /* cache entries bucketed by tile */
-  KD_KERNEL_TRANSPOSE = 9,  /* W^T and H_c^T copies for the backward GEMMs */
-  KD_KERNEL_COUNT = 10
+  KD_KERNEL_COUNT = 9
 };
 kd_status kd_profile_enable(uint32_t kernel_mask);
 kd_status kd_profile_read(int32_t kernel_id, double* total_ms, int64_t* launches);

@@ -23,7 +23,7 @@ _lib = None
 
 KERNELS = {
     "teacher": 0, "logits_fwd": 1, "combine": 2, "finalize": 3,
-    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7, "bucket": 8, "transpose": 9,
+    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7, "bucket": 8,
 }
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem size",

@@ -168,26 +168,22 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
   int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
   uint32_t* ent = reinterpret_cast<uint32_t*>(ws + p.off_ent);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
-  uint16_t* GT = reinterpret_cast<uint16_t*>(ws + p.off_gt);
-  uint16_t* WT = reinterpret_cast<uint16_t*>(ws + p.off_wt);
-  uint16_t* HT = reinterpret_cast<uint16_t*>(ws + p.off_ht);
   float* dhp = reinterpret_cast<float*>(ws + p.off_dhp);
   const float invT = 1.f / T;
   const float g_scale = float(1.0 / (double(N) * double(T)));
   const int ktiles = int(p.Vp / kd::gemm_bk());
   const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
 
-  // W^T [D, Vp] (zero past V) so that dH = G_c W reads vocab-contiguous rows
-  KD_LAUNCH(KD_KERNEL_TRANSPOSE, s,
-            kd::launch_transpose(W, D, int(V), int(D), WT, p.Vp, int(p.Vp), s));
-  // G_c^T and H_c^T of up to dw_group chunks sit side by side (ld = group *
-  // c_pad) and feed one dW GEMM with K = the group's positions.
-  const int64_t gt_ld = int64_t(p.dw_group) * p.c_pad;
-  const int bk = kd::gemm_bk();
+  // The G rows of up to dw_group consecutive chunks are kept one after
+  // another (position order, row stride Vp) and feed one dW GEMM with K = the
+  // group's positions; H rows of the group are consecutive in H already.
   int gj = 0;
+  int64_t group_row0 = 0;
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
     const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
     const int npt = (rows + kd::kTile - 1) / kd::kTile;
+    if (gj == 0) group_row0 = row0;
+    uint16_t* Gc = G + (row0 - group_row0) * p.Vp;
     kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
     KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
     kd::BucketArgs ba{topk_idx + row0 * K, rows, K, int(V), int(p.nvt), boff, ent};
@@ -210,25 +206,18 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
     la.p = pw;
     la.grad_loss = grad_loss;
     la.g_scale = g_scale;
-    la.G = G;
-    la.GT = GT;
-    la.gt_ld = gt_ld;
-    la.gt_col0 = int64_t(gj) * p.c_pad;
+    la.G = Gc;
     KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
-    kd::DhArgs da{G, WT, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
+    kd::DhArgs da{Gc, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
     KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
     if (p.dh_split > 1)
       KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
                 kd::launch_dh_reduce(dhp, p.dh_split, rows, int(D), p.c_pad, dH + row0 * D, s));
-    // H_c^T [D, c_pad] (zero past the chunk's rows) next to the group's others
-    KD_LAUNCH(KD_KERNEL_TRANSPOSE, s,
-              kd::launch_transpose(H + row0 * D, D, rows, int(D), HT + int64_t(gj) * p.c_pad, gt_ld,
-                                   int(p.c_pad), s));
     ++gj;
     const bool last = row0 + p.chunk >= N;
     if (gj == p.dw_group || last) {
-      const int kext = int((gj - 1) * p.c_pad + (rows + bk - 1) / bk * bk);
-      kd::DwArgs wa{GT, HT, kext, int(D), int(V), p.Vp, gt_ld, dW};
+      const int grows = int(row0 + rows - group_row0);
+      kd::DwArgs wa{G, H + group_row0 * D, grows, int(D), int(V), p.Vp, dW};
       KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
       gj = 0;
     }

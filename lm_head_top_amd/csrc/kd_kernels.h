@@ -45,9 +45,7 @@ struct LogitsArgs {
   const float* p;       // [c_pad, K]
   const float* grad_loss;  // device scalar or null
   float g_scale;        // 1 / (N T)
-  uint16_t* G;          // [c_pad, Vp] bf16
-  uint16_t* GT;         // [Vp, gt_ld] bf16: G^T of the chunk at columns gt_col0 ..
-  int64_t gt_ld, gt_col0;
+  uint16_t* G;          // [rows, Vp] bf16, offset to the chunk's first row (zero past V)
 };
 
 struct CombineArgs {
@@ -63,8 +61,8 @@ struct CombineArgs {
 };
 
 struct DhArgs {
-  const uint16_t* G;   // [c_pad, Vp]
-  const uint16_t* WT;  // [D, Vp] (transpose of W, zero past V)
+  const uint16_t* G;   // [rows, Vp], offset to the chunk's first row
+  const uint16_t* W;   // [V, D]
   int rows, D, V;
   int64_t Vp;
   int split;           // number of K splits
@@ -74,21 +72,20 @@ struct DhArgs {
   int64_t c_pad;
 };
 
-// dW += G^T H over a group of chunks whose G^T and H^T sit side by side.
+// dW += G^T H over a group of consecutive chunks (their G rows are stored
+// one after another, like their H rows).
 struct DwArgs {
-  const uint16_t* GT;  // [Vp, ld] (zero past the group's rows within kext)
-  const uint16_t* HT;  // [D, ld]
-  int kext;            // positions of the group, rounded up to the GEMM K step
+  const uint16_t* G;   // [rows, Vp], the group's first position
+  const uint16_t* H;   // [rows, D], the group's first position
+  int rows;            // positions in the group
   int D, V;
-  int64_t Vp, ld;
+  int64_t Vp;
   float* dW;           // [V, D]
 };
 
 int gemm_bk();  // K depth of one GEMM pipeline stage
 hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s);
-hipError_t launch_transpose(const uint16_t* src, int64_t ld_src, int R, int C, uint16_t* dst,
-                            int64_t ld_dst, int Rpad, hipStream_t s);
 hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -15,22 +15,23 @@
 //             forward: per-position tile max / sum-exp and the logits at the
 //                      cached ids go to small buffers (never the tile itself);
 //             backward: G = g/(N T) (exp(z - lse) - p scattered at the ids),
-//                      rounded to bf16 into G_c[c, V] and its transpose G_c^T;
+//                      rounded to bf16 into G_c[c, V];
 //   combine   forward: merge the vocab-tile partials into lse and KL per row;
-//   dh / dw   dH_c = G_c W (split over V, fp32 partials) and dW += G_c^T H_c.
+//   dh / dw   dH_c = G_c W (split over V, fp32 partials) and dW += G^T H over a
+//             group of chunks, reading G, W and H as they are stored.
 //
 // GEMM core: a 256 x 256 output tile per workgroup, split over waves 2 (M) x
 // WAVES/2 (N); each wave holds its (128 x 256/(WAVES/2)) part as 32x32 fp32
-// MFMA accumulators.  Both operands are K-contiguous in memory (the backward
-// keeps W^T, H_c^T and G_c^T copies so that every GEMM reads K-contiguous
-// rows).  Tiles of BK columns stream from HBM straight into LDS with
-// buffer_load_dwordx4 ... lds (no register staging; out-of-range rows and
-// columns read as zero), through a ring of STAGES buffers.  Inside a row of
-// the LDS tile the 16-byte chunks are XOR-swizzled by row so the MFMA
-// fragment reads (ds_read_b128, lanes on 32 consecutive rows at one k
-// offset) hit distinct banks.  A compute unit accepts one 1 KiB direct load
-// about every 20 cycles for all its waves together, so the loads are spread
-// between the MFMAs rather than issued in a burst.
+// MFMA accumulators.  Tiles of BK along K stream from HBM straight into LDS
+// with buffer_load_dwordx4 ... lds (no register staging; out-of-range rows
+// and columns read as zero), through a ring of STAGES buffers.  An operand
+// is either K-contiguous (W and H_c in the logits GEMM, G_c in dH): its LDS
+// tile is 256 rows of BK, 16-byte chunks XOR-swizzled by row, and a fragment
+// is one ds_read_b128; or k-major (W in dH, G and H in dW): its LDS tile is
+// BK rows of 256, 64-byte blocks XOR-swizzled by row, and a fragment is two
+// ds_read_b64_tr_b16, gfx950's transposing LDS read.  A compute unit accepts
+// one 1 KiB direct load about every 20 cycles for all its waves together, so
+// the loads are spread between the MFMAs rather than issued in a burst.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -205,42 +206,119 @@ struct DLoad {
   }
 };
 
+// Streams an operand stored k-major, X[k][m] (m contiguous, leading dimension
+// ld elements), into LDS tiles of BK rows (k) by 256 columns (m), 512 bytes a
+// row.  Load j of wave w fills rows 2(w*NI + j) and 2(w*NI + j) + 1: lane l
+// writes physical 16-byte chunk l%32 of row r = 2(w*NI + j) + l/32, which
+// holds the logical 64-byte block ((l%32)/4) ^ (r & 3) of that row (32
+// columns), so the transposing fragment reads below hit 64 distinct banks.
+// Columns at or past m_lim and rows at or past k_lim read as zero.
+struct MLoad {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[NI];  // byte offset of (row, this lane's columns) for k0 = 0, or kOOB
+  int kr[NI];         // tile row of this lane's chunk, per load
+  uint32_t ldb;       // row stride in bytes
+
+  __device__ __forceinline__ void init(const uint16_t* base, uint64_t bytes, int64_t ld, int m0,
+                                       int m_lim) {
+    const uint32_t nrec = bytes < uint64_t(kOOB) ? uint32_t(bytes) : kOOB;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, int(nrec), 0x00020000);
+    ldb = uint32_t(ld) * 2u;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane & 31;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = 2 * (wave * NI + j) + (lane >> 5);
+      kr[j] = r;
+      const int m = (((c >> 2) ^ (r & 3)) << 5) + (c & 3) * 8;
+      voff[j] = m0 + m < m_lim ? uint32_t((int64_t(r) * ld + m0 + m) * 2) : kOOB;
+    }
+  }
+
+  // Load j (of NI) of the BK x 256 tile at rows [k0, k0 + BK) into stage.
+  __device__ __forceinline__ void issue_one(int j, char* stage, int k0, int k_lim) const {
+    const int wave = threadIdx.x >> 6;
+    const uint32_t off = (voff[j] != kOOB && k0 + kr[j] < k_lim) ? voff[j] + uint32_t(k0) * ldb : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * NI + j) * 1024), 16, off,
+                                             0, 0, KD_LOAD_AUX);
+  }
+
+  __device__ __forceinline__ void issue(char* stage, int k0, int k_lim) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) issue_one(j, stage, k0, k_lim);
+  }
+};
+
+static_assert(OPER_BYTES == BK * 512, "a k-major tile holds BK rows of 256 bf16");
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// MFMA 32x32x16 operand fragment (lane l: column l%32, k = 8(l/32) .. +7) from
+// a k-major LDS tile: ds_read_b64_tr_b16 hands lane i of a 16-lane group the
+// 16-bit element i%4 of the 8 bytes addressed by lanes 4s + i/4 (s = 0..3).
+// Lane L of the group addresses row k0 + L/4, columns 4(L%4) .. +3, so lane i
+// receives rows k0 .. k0+3 of column i; two reads (rows +0 and +4) give 8 k.
+// `lane_off` is the lane's byte offset for block column 0 of step 0 without
+// the block swizzle (see mn_lane_off).
+__device__ __forceinline__ int mn_lane_off(int lane) {
+  const int gq = lane >> 4, i16 = lane & 15;
+  return (8 * (gq >> 1) + (i16 >> 2)) * 512 + (16 * (gq & 1) + 4 * (i16 & 3)) * 2;
+}
+
+__device__ __forceinline__ bf16x8 frag_mn(const char* tile, int col0, int s, int lane, int lane_off) {
+  // row & 3 of every row this lane addresses equals (lane & 15) >> 2
+  const int blk = (col0 >> 5) ^ ((lane & 15) >> 2);
+  const char* p = tile + s * (16 * 512) + lane_off + (blk << 6);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  const s16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 4 * 512));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // --------------------------------------------------------------- MFMA core ---
 
 // One BK-deep stage of the wave's WT_M x WT_N tile.  MFMA 32x32x16 operands:
-// lane l supplies row l % 32 and the 8 consecutive k of half l / 32.
+// lane l supplies row l % 32 and the 8 consecutive k of half l / 32; an
+// operand tile is row-major with k contiguous (AMN / BMN false, one
+// ds_read_b128 per fragment) or k-major (true, two transposing reads).
 // Fragments of the next 16-deep step load while the current step multiplies,
 // and the next stage's ring loads (2 * NI per wave) go out LPS per step, each
 // between two MFMAs.
+template <bool AMN, bool BMN, class LA, class LB>
 __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const char* __restrict__ sB,
                                           f32x16 (&acc)[MI][NJ], int wm, int wn, int lane,
-                                          const DLoad& la, const DLoad& lb, char* nst, int nk0,
+                                          const LA& la, const LB& lb, char* nst, int nk0,
                                           int ka_lim, int kb_lim) {
-  constexpr int NR = MI + NJ;  // fragment reads per step
-  constexpr int NQ = MI * NJ;  // MFMAs per step
-  const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31);  // tile rows are r31 mod 32
+  constexpr int NR = (AMN ? 2 : 1) * MI + (BMN ? 2 : 1) * NJ;  // fragment reads per step
+  constexpr int NQ = MI * NJ;                                  // MFMAs per step
+  const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31);   // K-contiguous tile rows are r31 mod 32
+  const int mo = mn_lane_off(lane);
   const char* pa = sA + (wm * WT_M + r31) * ROWB;
   const char* pb = sB + (wn * WT_N + r31) * ROWB;
+  auto read_a = [&](int i, int st) -> bf16x8 {
+    if constexpr (AMN) return frag_mn(sA, wm * WT_M + i * 32, st, lane, mo);
+    else return *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + (((2 * st + hi) ^ sw) * 16));
+  };
+  auto read_b = [&](int j, int st) -> bf16x8 {
+    if constexpr (BMN) return frag_mn(sB, wn * WT_N + j * 32, st, lane, mo);
+    else return *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + (((2 * st + hi) ^ sw) * 16));
+  };
   bf16x8 fa[2][MI], fb[2][NJ];
-  {
-    const int off = (hi ^ sw) * 16;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
+  for (int i = 0; i < MI; ++i) fa[0][i] = read_a(i, 0);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + off);
-  }
+  for (int j = 0; j < NJ; ++j) fb[0][j] = read_b(j, 0);
   __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // the first step's fragment reads
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int cur = s & 1;
     if (s + 1 < NS) {
-      const int off = ((2 * (s + 1) + hi) ^ sw) * 16;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-        fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + off);
+      for (int i = 0; i < MI; ++i) fa[cur ^ 1][i] = read_a(i, s + 1);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        fb[cur ^ 1][j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + off);
+      for (int j = 0; j < NJ; ++j) fb[cur ^ 1][j] = read_b(j, s + 1);
     }
     constexpr int NL = 2 * NI;
     const int l0 = s * LPS;
@@ -257,14 +335,17 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-    // NQ MFMAs; between them go the next step's fragment reads and this
-    // step's ring loads (spread evenly, or one after each of the first MFMAs)
+    // NQ MFMAs; between them go the next step's fragment reads (spread
+    // evenly) and this step's ring loads (one after each of the first MFMAs,
+    // or spread)
     const int nl = l0 < NL ? (NL - l0 < LPS ? NL - l0 : LPS) : 0;
     const int nr = s + 1 < NS ? NR : 0;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      const int rq = (nr * (q + 1)) / NQ - (nr * q) / NQ;
+#pragma unroll
+      for (int u = 0; u < rq; ++u) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (KD_VSPREAD ? (nl > 0 && q % (NQ / LPS) == 0 && q / (NQ / LPS) < nl) : (q < nl))
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
@@ -273,7 +354,8 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
 
 // acc[i][j] (wave (wm, wn) = (wave / WAVES_N, wave % WAVES_N)) register r holds C[m][n] with
 //   m = wm*WT_M + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*WT_N + j*32 + lane%32.
-__device__ __forceinline__ void gemm_core(const DLoad& la, const DLoad& lb, int k_begin, int k_end,
+template <bool AMN = false, bool BMN = false, class LA, class LB>
+__device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int k_begin, int k_end,
                                           int ka_lim, int kb_lim, f32x16 (&acc)[MI][NJ], char* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -301,8 +383,8 @@ __device__ __forceinline__ void gemm_core(const DLoad& la, const DLoad& lb, int 
     const int nxt = kt + STAGES - 1;
     const int nk0 = nxt < nk ? k_begin + nxt * BK : 0x3fffffff;
     const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    mma_stage(st, st + OPER_BYTES, acc, wm, wn, lane, la, lb, smem + (nxt % STAGES) * STAGE_BYTES, nk0,
-              ka_lim, kb_lim);
+    mma_stage<AMN, BMN>(st, st + OPER_BYTES, acc, wm, wn, lane, la, lb, smem + (nxt % STAGES) * STAGE_BYTES,
+                        nk0, ka_lim, kb_lim);
   }
   wait_vmcnt<0>();  // the trailing zero loads land before the epilogue reuses LDS
   lds_barrier();
@@ -567,7 +649,8 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
         }
       }
       __syncthreads();
-      // G_c rows: 128 positions x 256 vocab, bf16
+      // G_c rows: 128 positions x 256 vocab, bf16 (the dH and dW GEMMs both
+      // read this one copy)
 #pragma unroll 4
       for (int it = 0; it < 128 * 32 / GT; ++it) {
         const int pl = it * (GT / 32) + (tid >> 5);
@@ -583,19 +666,6 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
           o.w = bf16_rne(x1.z) | (bf16_rne(x1.w) << 16);
           *reinterpret_cast<uint4*>(a.G + int64_t(prow) * a.Vp + v0 + c8) = o;
         }
-      }
-      // G_c^T rows: 256 vocab x 128 positions, bf16 (positions past the chunk are 0)
-#pragma unroll 4
-      for (int it = 0; it < kTile * 16 / GT; ++it) {
-        const int vl = tid & (kTile - 1), pc = it * (GT / kTile) + tid / kTile;
-        const float* col = S + (pc * 8) * SLD + vl;
-        uint4 o;
-        o.x = bf16_rne(col[0]) | (bf16_rne(col[SLD]) << 16);
-        o.y = bf16_rne(col[2 * SLD]) | (bf16_rne(col[3 * SLD]) << 16);
-        o.z = bf16_rne(col[4 * SLD]) | (bf16_rne(col[5 * SLD]) << 16);
-        o.w = bf16_rne(col[6 * SLD]) | (bf16_rne(col[7 * SLD]) << 16);
-        *reinterpret_cast<uint4*>(a.GT + int64_t(v0 + vl) * a.gt_ld + a.gt_col0 + p0 + h * 128 +
-                                  pc * 8) = o;
       }
       __syncthreads();
     }
@@ -645,46 +715,6 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const float* __restrict__ 
   if (tid == 0) loss[0] = N > 0 ? float(red[0] / double(N)) : 0.f;
 }
 
-// --------------------------------------------------------------- transpose ---
-
-// dst[c][r] = src[r][c] for r < R, c < C; dst[c][r] = 0 for R <= r < Rpad.
-// 64 x 64 tiles through LDS.  C % 8 == 0, Rpad % 64 == 0, ld % 8 == 0.
-__global__ __launch_bounds__(NT) void transpose_kernel(const uint16_t* __restrict__ src, int64_t lds_,
-                                                       int R, int C, uint16_t* __restrict__ dst,
-                                                       int64_t ldd, int Rpad) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int q = u * NT + tid;  // 512 chunks of 8 elements
-    const int rr = q >> 3, cc = (q & 7) * 8;
-    const int r = r0 + rr, c = c0 + cc;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + int64_t(r) * lds_ + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[rr][cc + 2 * e] = uint16_t(w[e] & 0xffffu);
-      tile[rr][cc + 2 * e + 1] = uint16_t(w[e] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int q = u * NT + tid;
-    const int cc = q >> 3, rr = (q & 7) * 8;
-    const int c = c0 + cc, r = r0 + rr;
-    if (c < C && r < Rpad) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = uint32_t(tile[rr + 2 * e][cc]) | (uint32_t(tile[rr + 2 * e + 1][cc]) << 16);
-      *reinterpret_cast<uint4*>(dst + int64_t(c) * ldd + r) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
-}
-
 // --------------------------------------------------------------- dH and dW ---
 
 KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
@@ -700,11 +730,13 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
   if (k_end > a.Vp) k_end = int(a.Vp);
   f32x16 acc[MI][NJ];
   {
-    // A = G_c (positions x vocab), B = W^T (D x vocab); both vocab-contiguous
-    DLoad la, lb;
-    la.init(a.G, uint64_t(a.c_pad) * a.Vp * 2, a.Vp, tm * kTile, a.rows);
-    lb.init(a.WT, uint64_t(a.D) * a.Vp * 2, a.Vp, tn * kTile, a.D);
-    gemm_core(la, lb, k_begin, k_end, int(a.Vp), int(a.Vp), acc, smem);
+    // A = G_c (positions x vocab, vocab-contiguous); B = W read k-major
+    // (vocab rows, D contiguous) through the transposing fragment reads
+    DLoad la;
+    MLoad lb;
+    la.init(a.G, uint64_t(a.rows) * a.Vp * 2, a.Vp, tm * kTile, a.rows);
+    lb.init(a.W, uint64_t(a.V) * a.D * 2, a.D, tn * kTile, a.D);
+    gemm_core<false, true>(la, lb, k_begin, k_end, int(a.Vp), a.V, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -770,12 +802,12 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
 #endif
   f32x16 acc[MI][NJ];
   {
-    // A = G^T (vocab x positions), B = H^T (D x positions) of the chunk group;
-    // both position-contiguous and zero past the group's last row
-    DLoad la, lb;
-    la.init(a.GT, uint64_t(a.Vp) * a.ld * 2, a.ld, tm * kTile, a.V);
-    lb.init(a.HT, uint64_t(a.D) * a.ld * 2, a.ld, tn * kTile, a.D);
-    gemm_core(la, lb, 0, a.kext, a.kext, a.kext, acc, smem);
+    // A = G^T and B = H^T of the chunk group, both read k-major from G
+    // (positions x vocab) and H (positions x D) as they are stored
+    MLoad la, lb;
+    la.init(a.G, uint64_t(a.rows) * a.Vp * 2, a.Vp, tm * kTile, int(a.Vp));
+    lb.init(a.H, uint64_t(a.rows) * a.D * 2, a.D, tn * kTile, a.D);
+    gemm_core<true, true>(la, lb, 0, a.rows, a.rows, a.rows, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -855,13 +887,6 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 
 hipError_t launch_finalize(const float* rowkl, int64_t N, float* loss, hipStream_t s) {
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(NT), 0, s, rowkl, N, loss);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const uint16_t* src, int64_t ld_src, int R, int C, uint16_t* dst,
-                            int64_t ld_dst, int Rpad, hipStream_t s) {
-  hipLaunchKernelGGL(transpose_kernel, dim3(unsigned(ceil_div(C, 64)), unsigned(ceil_div(Rpad, 64))),
-                     dim3(NT), 0, s, src, ld_src, R, C, dst, ld_dst, Rpad);
   return hipGetLastError();
 }
 

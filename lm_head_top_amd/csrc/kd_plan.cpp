@@ -65,8 +65,9 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
   p.npt = p.c_pad / kTile;
   p.dh_split = dh_split_for(c, D);
   p.dw_group = dw_group_for(c, N);
-  // every GEMM operand is addressed with 32-bit buffer offsets
-  if (p.dw_group * p.c_pad * p.Vp > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
+  // every GEMM operand is addressed with 32-bit buffer offsets (bf16)
+  if (p.dw_group * c * p.Vp > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
+  if (p.dw_group * c * D > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
   if (V * D > (int64_t(1) << 31) - 64 || p.Vp * D > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
   // the fp32 dW accumulator is read through a buffer descriptor as well
   if (V * D * 4 > (int64_t(1) << 32) - 64) return KD_ERR_UNSUPPORTED;
@@ -91,10 +92,8 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
   const size_t fwd_end = off;
   // backward-only region aliases the forward-only one
   off = shared_end;
-  p.off_g = take(size_t(p.c_pad) * p.Vp * 2);
-  p.off_gt = take(size_t(p.Vp) * p.dw_group * p.c_pad * 2);
-  p.off_wt = take(size_t(D) * p.Vp * 2);
-  p.off_ht = take(size_t(D) * p.dw_group * p.c_pad * 2);
+  // G rows of a group of dw_group consecutive chunks, in position order
+  p.off_g = take(size_t(p.dw_group) * c * p.Vp * 2);
   p.off_dhp = take(p.dh_split > 1 ? size_t(p.dh_split) * p.c_pad * D * 4 : 0);
   const size_t bwd_end = off;
   p.bytes = fwd_end > bwd_end ? fwd_end : bwd_end;

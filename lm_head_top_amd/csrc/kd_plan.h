@@ -25,11 +25,11 @@ struct Plan {
   int64_t Vp = 0;      // V rounded up to kTile (row stride of G_c)
   int64_t npt = 0;     // position tiles per chunk
   int dh_split = 1;    // split-K factor of the dH GEMM
-  int dw_group = 1;    // chunks whose G^T and H^T feed one dW GEMM (K = dw_group * chunk)
+  int dw_group = 1;    // consecutive chunks whose G rows feed one dW GEMM (K = dw_group * chunk)
   // workspace byte offsets
   size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0;  // shared by fwd and bwd
   size_t off_pm = 0, off_ps = 0, off_zsel = 0, off_rowkl = 0;  // forward only
-  size_t off_g = 0, off_gt = 0, off_wt = 0, off_ht = 0, off_dhp = 0;  // backward only (aliases forward)
+  size_t off_g = 0, off_dhp = 0;  // backward only (aliases forward)
   size_t bytes = 0;
 };
 

@@ -158,10 +158,10 @@ def test_validate_rejects(lib):
 def test_profile_api(lib):
     ms = ctypes.c_double()
     n = ctypes.c_int64()
-    assert lib.kd_profile_enable(1 << 10) == KD_ERR_INVALID_ARG
+    assert lib.kd_profile_enable(1 << 9) == KD_ERR_INVALID_ARG
     assert lib.kd_profile_read(-1, ctypes.byref(ms), ctypes.byref(n)) == KD_ERR_INVALID_ARG
     assert lib.kd_profile_enable(0) == KD_OK
-    assert lib.kd_profile_enable(0x3FF) == KD_OK
+    assert lib.kd_profile_enable(0x1FF) == KD_OK
     assert lib.kd_profile_enable(0) == KD_OK
     assert lib.kd_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == KD_OK
     assert n.value == 0 and ms.value == 0.0
