@@ -56,9 +56,6 @@
 #ifndef KD_LOAD_AUX
 #define KD_LOAD_AUX 0
 #endif
-#ifndef KD_DW_BAND
-#define KD_DW_BAND 0
-#endif
 
 namespace kd {
 namespace {
@@ -783,23 +780,7 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
   const int tiles_m = int((a.V + kTile - 1) / kTile);
   const int tiles_n = (a.D + kTile - 1) / kTile;
   const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-#if KD_DW_BAND
-  // bands of KD_DW_BAND output-column tiles; inside a band, vocab-tile major
-  constexpr int GN = KD_DW_BAND;
-  const int nb = tiles_n / GN;
-  int tm, tn;
-  if (tile < nb * GN * tiles_m) {
-    const int band = tile / (GN * tiles_m), r = tile - band * GN * tiles_m;
-    tm = r / GN;
-    tn = band * GN + (r - tm * GN);
-  } else {
-    const int w = tiles_n - nb * GN, r = tile - nb * GN * tiles_m;
-    tm = r / w;
-    tn = nb * GN + (r - tm * w);
-  }
-#else
   const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
-#endif
   f32x16 acc[MI][NJ];
   {
     // A = G^T and B = H^T of the chunk group, both read k-major from G
