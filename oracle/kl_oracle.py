@@ -31,10 +31,11 @@ For positions n in [0, N), vocabulary entries v in [0, V) and cache slots k in
         G[n, v] = g / (N T) * (exp(z[n, v] - lse[n]) - sum_{k: idx[n,k] = v} p[n, k])
   7. dH = G W   (N x D)   and   dW = dW_in + G^T H   (V x D)
 
-Readings of points the pages leave open (KL direction, renormalisation over K,
-temperature on both sides with no T^2 factor, mean over all N positions, no
-student-side renormalisation, duplicate ids as scatter-add, -inf teacher
-logits as p = 0) are listed in DESIGN.md under "Readings".
+Where the pages leave a point open this oracle reads it as: forward KL
+(teacher || student); the teacher renormalised over its K cached entries; the
+temperature on both sides with no T^2 factor; the mean over all N positions;
+no student-side renormalisation; duplicate ids as a scatter-add; a -inf
+teacher logit as p = 0.
 
 Parity pins: every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (Gibbs inequality, KL = 0 special case, shift
