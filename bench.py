@@ -39,7 +39,8 @@ KERNEL_SOURCES = ("lm_head_top_amd/csrc/kd_kernels.hip", "lm_head_top_amd/csrc/k
 KERNEL_PATTERNS = (("logits_kernel<0>", "logits_fwd"), ("logits_kernel<1>", "logits_bwd"),
                    ("dh_reduce_kernel", "dh_reduce"), ("dh_kernel", "dh"), ("dw_kernel", "dw"),
                    ("teacher_kernel", "teacher"), ("bucket_kernel", "bucket"),
-                   ("combine_kernel", "combine"), ("finalize_kernel", "finalize"))
+                   ("combine_kernel", "combine"), ("finalize_kernel", "finalize"),
+                   ("topk_select_kernel", "topk_select"))
 COPY_KERNEL_PATTERN = "neg_kernel"   # torch.neg(fp32): reads and writes the calibration bytes once
 
 
@@ -321,6 +322,52 @@ def dense_reference(args):
     print(json.dumps(line), flush=True)
 
 
+def topk_writer(args):
+    """Teacher top-K cache writer on teacher logits of the workload's shape
+    (N x V, fp32 or bf16, drawn on the device from a seeded generator): time
+    per call and HBM bandwidth against the 8 TB/s roofline (the logits are read
+    once; the cache written is N * K * 8 bytes)."""
+    import torch
+    import lm_head_top_amd as kd
+    from synth import get_config
+    kd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    N, V, K = cfg.N, cfg.V, cfg.K
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    x = torch.randn((N, V), generator=g, device=dev) * 3 ** 0.5
+    if args.topk_dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    esz = x.element_size()
+    for _ in range(args.warmup):
+        kd.topk_select(x, K)
+    kd.profile_enable(("topk_select",))
+    kd.profile_read("topk_select")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        idx, val = kd.topk_select(x, K)
+    e1.record()
+    torch.cuda.synchronize()
+    kd.profile_enable(None)
+    ms, n = kd.profile_read("topk_select")
+    avg = ms / max(n, 1)
+    bytes_call = N * V * esz + N * K * 8
+    gbs = bytes_call / (avg * 1e-3) / 1e9
+    line = {"mode": "topk_writer", "metric": "teacher top-K cache writer rows/s", "unit": "rows/s",
+            "value": round(N / (e0.elapsed_time(e1) / args.steps * 1e-3), 1),
+            "ms_per_call": round(e0.elapsed_time(e1) / args.steps, 4), "steps": args.steps,
+            "dtype": args.topk_dtype, "config": {"workload": f"teacher logits of {WORKLOAD_NAMES[cfg.name]}",
+                                                 "N": N, "V": V, "K": K, "seed": args.seed},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(gbs / 8000.0, 4), "traffic": None,
+                         "avg_launch_ms": round(avg, 4), "bytes_per_launch": bytes_call}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,11 +397,19 @@ def main():
     ap.add_argument("--dense-reference", action="store_true",
                     help="plain PyTorch dense loss beside the fused one on --config "
                          "(peak memory, time)")
+    ap.add_argument("--topk-writer", action="store_true",
+                    help="time the teacher top-K cache writer on N x V teacher logits of --config")
+    ap.add_argument("--topk-dtype", default="f32", choices=("f32", "bf16"))
     args = ap.parse_args()
-    if args.memory_sweep or args.dense_reference:
+    if args.memory_sweep or args.dense_reference or args.topk_writer:
         if args.gpus != 1:
             sys.exit(2)
-        (memory_sweep if args.memory_sweep else dense_reference)(args)
+        if args.memory_sweep:
+            memory_sweep(args)
+        elif args.dense_reference:
+            dense_reference(args)
+        else:
+            topk_writer(args)
         return
     if args.stats_from:
         line = None

@@ -133,6 +133,29 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W,
 kd_status kd_topk_kl_validate(const int32_t* topk_idx, int64_t N, int32_t K,
                               int64_t V, int32_t* d_flags, void* hip_stream);
 
+/*
+ * Teacher top-K cache writer (the offline step before the loss: the teacher
+ * runs once and its K largest logits per position are kept; "Distilling an
+ * LLM on One GPU", section "The two changes"; "The $250GB Memory Spike That
+ * Killed Distillation Projects Is Now Optional", section "Offline Top-K").
+ *
+ *   logits      [N, V] teacher logits, dtype KD_DTYPE_F32 (float) or
+ *               KD_DTYPE_BF16 (uint16_t bf16 bit patterns), row-major
+ *   topk_idx    int32 [N, K] out: token ids, best first
+ *   topk_logit  fp32  [N, K] out: their logits (bf16 widened exactly; -0.0 is
+ *               written as +0.0)
+ *
+ * Order: larger logit first; equal logits (-0.0 equals +0.0) by lower id, so
+ * the result is unique.  NaN logits are outside the contract (memory-safe,
+ * result unspecified).  1 <= K <= min(V, KD_MAX_K); V <= 2^31 - 1.  One pass
+ * over the logits; no workspace.  Alignment: 4 bytes (fp32) or 2 bytes (bf16);
+ * rows whose byte length is a multiple of 16 with a 16-byte aligned base are
+ * read with 16-byte loads.  Output rows are written in full.
+ */
+enum { KD_DTYPE_F32 = 0, KD_DTYPE_BF16 = 1 };
+kd_status kd_topk_select(const void* logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
+                         int32_t* topk_idx, float* topk_logit, void* hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char* kd_status_string(kd_status s);
 
@@ -161,7 +184,8 @@ enum {
   KD_KERNEL_DH_REDUCE = 6,  /* sum of the dH split partials */
   KD_KERNEL_DW = 7,         /* dW += G^T H */
   KD_KERNEL_BUCKET = 8,     /* cache entries bucketed by tile */
-  KD_KERNEL_COUNT = 9
+  KD_KERNEL_TOPK_SELECT = 9, /* teacher top-K cache writer */
+  KD_KERNEL_COUNT = 10
 };
 kd_status kd_profile_enable(uint32_t kernel_mask);
 kd_status kd_profile_read(int32_t kernel_id, double* total_ms, int64_t* launches);

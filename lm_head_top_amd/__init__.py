@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "lib_path", "load_library", "workspace_size", "forward", "backward", "validate",
-    "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError",
+    "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError", "topk_select",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,7 +23,7 @@ _lib = None
 
 KERNELS = {
     "teacher": 0, "logits_fwd": 1, "combine": 2, "finalize": 3,
-    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7, "bucket": 8,
+    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7, "bucket": 8, "topk_select": 9,
 }
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem size",
@@ -72,6 +72,8 @@ def load_library():
     lib.kd_topk_kl_validate.restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
+    lib.kd_topk_select.argtypes = [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]
+    lib.kd_topk_select.restype = ctypes.c_int
     lib.kd_last_hip_error.argtypes = []
     lib.kd_last_hip_error.restype = ctypes.c_char_p
     lib.kd_profile_enable.argtypes = [ctypes.c_uint32]
@@ -171,6 +173,27 @@ def backward(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0,
         float(T), int(chunk), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
     _check(st, "kd_topk_kl_backward")
     return dH, dW
+
+
+def topk_select(logits, K: int):
+    """Teacher top-K cache of fp32 or bf16 logits [N, V]: (ids int32 [N, K],
+    logits fp32 [N, K]), best first, equal logits by lower id."""
+    torch = _torch()
+    if not logits.is_cuda or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous device tensor [N, V]")
+    if logits.dtype == torch.float32:
+        dtype = 0
+    elif logits.dtype == torch.bfloat16:
+        dtype = 1
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    N, V = logits.shape
+    idx = torch.empty((N, K), dtype=torch.int32, device=logits.device)
+    val = torch.empty((N, K), dtype=torch.float32, device=logits.device)
+    st = load_library().kd_topk_select(_ptr(logits), dtype, N, V, int(K), _ptr(idx), _ptr(val),
+                                       _stream_ptr(torch, logits.device))
+    _check(st, "kd_topk_select")
+    return idx, val
 
 
 def validate(topk_idx, V: int) -> int:

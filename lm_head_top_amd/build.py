@@ -19,7 +19,7 @@ LIB_NAME = "libkdtopk.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-HIP_SOURCES = ["kd_kernels.hip", "kd_capi.hip"]
+HIP_SOURCES = ["kd_kernels.hip", "kd_topk_select.hip", "kd_capi.hip"]
 HOST_SOURCES = ["kd_plan.cpp"]
 
 # Packed-FP32 VALU ops are disabled for all device code.

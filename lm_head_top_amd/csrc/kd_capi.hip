@@ -236,6 +236,21 @@ kd_status kd_topk_kl_validate(const int32_t* topk_idx, int64_t N, int32_t K, int
   return KD_OK;
 }
 
+kd_status kd_topk_select(const void* logits, int32_t dtype, int64_t N, int64_t V, int32_t K,
+                         int32_t* topk_idx, float* topk_logit, void* hip_stream) {
+  if (dtype != KD_DTYPE_F32 && dtype != KD_DTYPE_BF16) return KD_ERR_INVALID_ARG;
+  if (N < 0 || V <= 0 || K <= 0 || K > V) return KD_ERR_INVALID_ARG;
+  if (K > KD_MAX_K || V > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1) return KD_ERR_UNSUPPORTED;
+  const size_t esz = dtype == KD_DTYPE_F32 ? 4 : 2;
+  if (N == 0) return KD_OK;
+  if (bad_ptr(logits, esz) || bad_ptr(topk_idx, 4) || bad_ptr(topk_logit, 4)) return KD_ERR_INVALID_ARG;
+  const bool vec = (V * int64_t(esz)) % 16 == 0 && kd::aligned(logits, 16);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  KD_LAUNCH(KD_KERNEL_TOPK_SELECT, s,
+            kd::launch_topk_select(logits, dtype, vec, N, V, K, topk_idx, topk_logit, s));
+  return KD_OK;
+}
+
 kd_status kd_profile_enable(uint32_t kernel_mask) {
   if (kernel_mask >> KD_KERNEL_COUNT) return KD_ERR_INVALID_ARG;
   std::lock_guard<std::mutex> lk(g_prof_mu);

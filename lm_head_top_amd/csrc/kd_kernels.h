@@ -98,4 +98,9 @@ hipError_t launch_validate(const int32_t* idx, int64_t N, int K, int64_t V, int3
                            hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 
+// Teacher top-K cache writer: one workgroup per row of logits [N, V] (dtype 0
+// fp32, 1 bf16; vec: 16-byte loads allowed).
+hipError_t launch_topk_select(const void* logits, int dtype, bool vec, int64_t N, int64_t V, int K,
+                              int32_t* idx, float* val, hipStream_t s);
+
 }  // namespace kd

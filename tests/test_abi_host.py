@@ -158,10 +158,10 @@ def test_validate_rejects(lib):
 def test_profile_api(lib):
     ms = ctypes.c_double()
     n = ctypes.c_int64()
-    assert lib.kd_profile_enable(1 << 9) == KD_ERR_INVALID_ARG
+    assert lib.kd_profile_enable(1 << 10) == KD_ERR_INVALID_ARG
     assert lib.kd_profile_read(-1, ctypes.byref(ms), ctypes.byref(n)) == KD_ERR_INVALID_ARG
     assert lib.kd_profile_enable(0) == KD_OK
-    assert lib.kd_profile_enable(0x1FF) == KD_OK
+    assert lib.kd_profile_enable(0x3FF) == KD_OK
     assert lib.kd_profile_enable(0) == KD_OK
     assert lib.kd_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == KD_OK
     assert n.value == 0 and ms.value == 0.0
@@ -192,3 +192,18 @@ def test_one_hip_runtime_in_the_process():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+def test_topk_select_rejects(lib):
+    vp = ctypes.c_void_p
+    ok = vp(256)
+    f = lib.kd_topk_select
+    assert f(ok, 2, 4, 100, 10, ok, ok, None) == KD_ERR_INVALID_ARG      # dtype
+    assert f(ok, 0, 4, 100, 101, ok, ok, None) == KD_ERR_INVALID_ARG     # K > V
+    assert f(ok, 0, 4, 100, 0, ok, ok, None) == KD_ERR_INVALID_ARG       # K = 0
+    assert f(ok, 0, -1, 100, 10, ok, ok, None) == KD_ERR_INVALID_ARG     # N < 0
+    assert f(ok, 0, 4, 1000, 257, ok, ok, None) == KD_ERR_UNSUPPORTED    # K > KD_MAX_K
+    assert f(ok, 0, 4, 1 << 31, 10, ok, ok, None) == KD_ERR_UNSUPPORTED  # V >= 2^31
+    assert f(vp(2), 0, 4, 100, 10, ok, ok, None) == KD_ERR_INVALID_ARG   # fp32 needs 4-byte alignment
+    assert f(None, 1, 4, 100, 10, ok, ok, None) == KD_ERR_INVALID_ARG    # null logits
+    assert f(None, 0, 0, 100, 10, None, None, None) == KD_OK             # empty: nothing to do
