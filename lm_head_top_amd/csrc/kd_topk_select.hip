@@ -24,10 +24,17 @@
 namespace kd {
 namespace {
 
-constexpr int TS = 256;                  // threads per row
-constexpr int PER_IT = 2048;             // logits per batch (8 per thread)
-constexpr int CAP = 4096;                // candidate keys in LDS (32 KiB): 4 rows per CU
+#ifndef KD_TOPK_THREADS
+#define KD_TOPK_THREADS 256
+#endif
+#ifndef KD_TOPK_BATCH
+#define KD_TOPK_BATCH 2048
+#endif
+constexpr int TS = KD_TOPK_THREADS;      // threads per row
+constexpr int PER_IT = KD_TOPK_BATCH;    // logits per batch
+constexpr int CAP = 2 * PER_IT;          // candidate keys in LDS (32 KiB at 2048: 4 rows per CU)
 static_assert(CAP >= 2 * PER_IT && CAP - PER_IT >= 256, "a batch must fit beside a full list");
+static_assert(PER_IT % (TS * 8) == 0, "a batch is whole 16-byte loads of bf16 for every thread");
 
 // Order-preserving 32-bit image of a float with -0.0 taken as +0.0.
 __device__ __forceinline__ uint32_t sortable(float x) {
@@ -179,10 +186,10 @@ __global__ __launch_bounds__(TS) void topk_select_kernel(const void* __restrict_
     }
   }
   n = compact(cand, n, K);
-  if (tid < n) {
-    const uint64_t key = cand[tid];
-    out_idx[row * K + tid] = int32_t(~uint32_t(key));
-    out_val[row * K + tid] = unsortable(uint32_t(key >> 32));
+  for (int i = tid; i < n; i += TS) {
+    const uint64_t key = cand[i];
+    out_idx[row * K + i] = int32_t(~uint32_t(key));
+    out_val[row * K + i] = unsortable(uint32_t(key >> 32));
   }
 }
 
