@@ -368,6 +368,62 @@ def topk_writer(args):
     print(json.dumps(line), flush=True)
 
 
+def keep_compare(args):
+    """The fused loss (recomputes each chunk in the backward, 8 N D V flops,
+    O(chunk V) memory) beside the kept-gradient comparator (keeps G for the
+    backward, 6 N D V flops, O(N V) memory) on the same inputs: time of one
+    forward + backward and peak memory.  A measurement aid."""
+    import torch
+    import lm_head_top_amd as kd
+    from synth import get_config
+    kd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    N, D, V, K, T, chunk = cfg.N, cfg.D, cfg.V, cfg.K, cfg.T, cfg.chunk
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    W = (torch.randn((V, D), generator=g, device=dev) * D ** -0.5).to(torch.bfloat16)
+    H, idx, t = _gpu_inputs(torch, N, D, V, K, args.seed + 1, dev)
+    dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
+
+    def fused():
+        loss, lse = kd.forward(H, W, idx, t, T, chunk)
+        kd.backward(H, W, idx, t, lse, None, T, chunk, dW=dW)
+        return loss
+
+    def keep():
+        loss, lse, ws = kd.forward_keep(H, W, idx, t, T, chunk)
+        kd.backward_keep(H, W, K, ws, None, T, chunk, dW=dW)
+        return loss
+
+    out = {}
+    for name, fn in (("fused", fused), ("kept_gradient", keep)):
+        fn()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        times = []
+        for _ in range(max(args.steps, 1)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            loss = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        out[name] = {"ms_median": round(times[len(times) // 2], 3),
+                     "peak_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
+                     "loss": float(loss.item())}
+        log(f"{name}: {out[name]}")
+    line = {"mode": "kept_gradient_compare",
+            "config": {"workload": WORKLOAD_NAMES[cfg.name], "N": N, "D": D, "V": V, "K": K,
+                       "chunk": chunk, "seed": args.seed}, **out,
+            "time_ratio_fused_over_kept": round(out["fused"]["ms_median"] / out["kept_gradient"]["ms_median"], 3),
+            "memory_ratio_kept_over_fused": round(out["kept_gradient"]["peak_gib"] / out["fused"]["peak_gib"], 3)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,7 +456,14 @@ def main():
     ap.add_argument("--topk-writer", action="store_true",
                     help="time the teacher top-K cache writer on N x V teacher logits of --config")
     ap.add_argument("--topk-dtype", default="f32", choices=("f32", "bf16"))
+    ap.add_argument("--keep-compare", action="store_true",
+                    help="the fused loss beside the kept-gradient comparator on --config")
     args = ap.parse_args()
+    if args.keep_compare:
+        if args.gpus != 1:
+            sys.exit(2)
+        keep_compare(args)
+        return
     if args.memory_sweep or args.dense_reference or args.topk_writer:
         if args.gpus != 1:
             sys.exit(2)

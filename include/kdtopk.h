@@ -126,6 +126,34 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W,
                               void* hip_stream);
 
 /*
+ * Kept-gradient comparator (the "forward-chunked" variant the pages compare
+ * against: it keeps what the backward needs instead of recomputing it; "The
+ * $250GB Memory Spike That Killed Distillation Projects Is Now Optional",
+ * section "What a Single H200 GPU Can Now Do"; "Distilling an LLM on One
+ * GPU", section "What this changes in practice").  Same loss and gradients
+ * as the entry points above, 6 N D V flops instead of 8, memory O(N V):
+ *
+ *   kd_topk_kl_forward_keep    as kd_topk_kl_forward (same outputs), and it
+ *                              also leaves G / g for all N positions (bf16)
+ *                              in the workspace;
+ *   kd_topk_kl_backward_keep   dH = g G W (overwritten) and dW += g G^T H from
+ *                              that workspace; g = *grad_loss or 1.
+ *
+ * The workspace (kd_topk_kl_keep_workspace_size bytes, 256-byte aligned,
+ * caller-owned) must be the one the forward filled, with the same sizes; it is
+ * N * V * 2 bytes plus a chunk's fp32 logits and the forward's buffers.
+ */
+size_t kd_topk_kl_keep_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int64_t chunk);
+kd_status kd_topk_kl_forward_keep(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                  const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                                  float T, int64_t chunk, float* loss, float* lse, float* row_kl,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream);
+kd_status kd_topk_kl_backward_keep(const uint16_t* H, const uint16_t* W, const float* grad_loss,
+                                   int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                                   uint16_t* dH, float* dW, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream);
+
+/*
  * Debug aid, not on the hot path: checks the teacher cache's ids.
  * d_flags (device int32 [1]) is overwritten with bit 0 set if some id lies
  * outside [0, V) and bit 1 set if some row holds an id twice.
@@ -185,7 +213,8 @@ enum {
   KD_KERNEL_DW = 7,         /* dW += G^T H */
   KD_KERNEL_BUCKET = 8,     /* cache entries bucketed by tile */
   KD_KERNEL_TOPK_SELECT = 9, /* teacher top-K cache writer */
-  KD_KERNEL_COUNT = 10
+  KD_KERNEL_KEEP_GRAD = 10, /* kept-gradient mode: G of a chunk from its kept logits */
+  KD_KERNEL_COUNT = 11
 };
 kd_status kd_profile_enable(uint32_t kernel_mask);
 kd_status kd_profile_read(int32_t kernel_id, double* total_ms, int64_t* launches);

@@ -15,6 +15,7 @@ import os
 __all__ = [
     "lib_path", "load_library", "workspace_size", "forward", "backward", "validate",
     "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError", "topk_select",
+    "keep_workspace_size", "forward_keep", "backward_keep",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,7 +24,7 @@ _lib = None
 
 KERNELS = {
     "teacher": 0, "logits_fwd": 1, "combine": 2, "finalize": 3,
-    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7, "bucket": 8, "topk_select": 9,
+    "logits_bwd": 4, "dh": 5, "dh_reduce": 6, "dw": 7, "bucket": 8, "topk_select": 9, "keep_grad": 10,
 }
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem size",
@@ -72,6 +73,13 @@ def load_library():
     lib.kd_topk_kl_validate.restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
+    lib.kd_topk_kl_keep_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i64]
+    lib.kd_topk_kl_keep_workspace_size.restype = c_sz
+    lib.kd_topk_kl_forward_keep.argtypes = lib.kd_topk_kl_forward.argtypes
+    lib.kd_topk_kl_forward_keep.restype = ctypes.c_int
+    lib.kd_topk_kl_backward_keep.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_f, c_i64,
+                                             c_vp, c_vp, c_vp, c_sz, c_vp]
+    lib.kd_topk_kl_backward_keep.restype = ctypes.c_int
     lib.kd_topk_select.argtypes = [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]
     lib.kd_topk_select.restype = ctypes.c_int
     lib.kd_last_hip_error.argtypes = []
@@ -172,6 +180,52 @@ def backward(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0,
         _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), _ptr(lse), _ptr(gl), N, D, V, K,
         float(T), int(chunk), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
     _check(st, "kd_topk_kl_backward")
+    return dH, dW
+
+
+def keep_workspace_size(N: int, D: int, V: int, K: int, chunk: int) -> int:
+    return int(load_library().kd_topk_kl_keep_workspace_size(N, D, V, K, chunk))
+
+
+def forward_keep(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024,
+                 want_row_kl: bool = False, workspace=None):
+    """Kept-gradient comparator: the forward's outputs plus the workspace
+    holding G for every position, which backward_keep consumes.  Returns
+    (loss, lse[, row_kl], workspace)."""
+    torch = _torch()
+    N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
+    dev = H.device
+    need = keep_workspace_size(N, D, V, K, chunk)
+    if need == 0:
+        raise KDError(1, "keep_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(N, dtype=torch.float32, device=dev) if want_row_kl else None
+    st = load_library().kd_topk_kl_forward_keep(
+        _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), N, D, V, K, float(T), int(chunk),
+        _ptr(loss), _ptr(lse), _ptr(row_kl), _ptr(workspace), workspace.numel(),
+        _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_forward_keep")
+    return ((loss, lse, row_kl) if want_row_kl else (loss, lse)) + (workspace,)
+
+
+def backward_keep(H, W, K: int, workspace, grad_loss=None, T: float = 1.0, chunk: int = 1024,
+                  dW=None):
+    """dH (overwritten) and dW (accumulated) from a forward_keep workspace."""
+    torch = _torch()
+    N, D = H.shape
+    V = W.shape[0]
+    dev = H.device
+    dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    if dW is None:
+        dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
+    gl = grad_loss.contiguous() if grad_loss is not None else None
+    st = load_library().kd_topk_kl_backward_keep(
+        _ptr(H), _ptr(W), _ptr(gl), N, D, V, int(K), float(T), int(chunk), _ptr(dH), _ptr(dW),
+        _ptr(workspace), workspace.numel(), _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_backward_keep")
     return dH, dW
 
 

@@ -83,26 +83,16 @@ size_t kd_topk_kl_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int
   return p.bytes;
 }
 
-kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
-                             const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
-                             float T, int64_t chunk, float* loss, float* lse, float* row_kl,
-                             void* workspace, size_t workspace_bytes, void* hip_stream) {
-  kd::Plan p;
-  const kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
-  if (st != KD_OK) return st;
-  if (bad_ptr(loss, 4)) return KD_ERR_INVALID_ARG;
-  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(topk_idx, 4) ||
-                bad_ptr(topk_logit, 4) || bad_ptr(lse, 4)))
-    return KD_ERR_INVALID_ARG;
-  if (row_kl != nullptr && !kd::aligned(row_kl, 4)) return KD_ERR_INVALID_ARG;
-  if (N > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return KD_ERR_WORKSPACE;
-  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (N == 0) {
-    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
-    return KD_OK;
-  }
-  char* ws = static_cast<char*>(workspace);
+}  // extern "C"
+
+namespace {
+
+// The forward's chunk loop.  With zkeep / gall set (kept-gradient mode) each
+// chunk's fp32 logits are kept and turned into its G rows of gall.
+kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                      const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K, float T,
+                      float* loss, float* lse, float* row_kl, char* ws, float* zkeep, uint16_t* gall,
+                      hipStream_t s) {
   float* pw = reinterpret_cast<float*>(ws + p.off_p);
   float* hw = reinterpret_cast<float*>(ws + p.off_h);
   int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
@@ -112,6 +102,7 @@ kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W, const int32_t
   float* zsel = reinterpret_cast<float*>(ws + p.off_zsel);
   float* rowkl = row_kl != nullptr ? row_kl : reinterpret_cast<float*>(ws + p.off_rowkl);
   const float invT = 1.f / T;
+  const float g_scale = float(1.0 / (double(N) * double(T)));
 
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
     const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
@@ -134,14 +125,119 @@ kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W, const int32_t
     la.invT = invT;
     la.boff = boff;
     la.ent = ent;
+    la.zkeep = zkeep;
     la.pm = pm;
     la.ps = ps;
     la.zsel = zsel;
     KD_LAUNCH(KD_KERNEL_LOGITS_FWD, s, kd::launch_logits_fwd(la, s));
     kd::CombineArgs ca{pm, ps, zsel, pw, hw, rows, K, int(p.nvt), p.c_pad, lse + row0, rowkl + row0};
     KD_LAUNCH(KD_KERNEL_COMBINE, s, kd::launch_combine(ca, s));
+    if (zkeep != nullptr)
+      KD_LAUNCH(KD_KERNEL_KEEP_GRAD, s,
+                kd::launch_keep_grad(zkeep, lse + row0, topk_idx + row0 * K, pw, rows, K, int(V), p.Vp,
+                                     g_scale, gall + row0 * p.Vp, s));
   }
   KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, N, loss, s));
+  return KD_OK;
+}
+
+kd_status check_forward_args(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                             const float* topk_logit, int64_t N, float* loss, float* lse, float* row_kl,
+                             void* workspace, size_t workspace_bytes, size_t need) {
+  if (bad_ptr(loss, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(topk_idx, 4) ||
+                bad_ptr(topk_logit, 4) || bad_ptr(lse, 4)))
+    return KD_ERR_INVALID_ARG;
+  if (row_kl != nullptr && !kd::aligned(row_kl, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (workspace == nullptr || workspace_bytes < need)) return KD_ERR_WORKSPACE;
+  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
+  (void)p;
+  return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                             const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                             float T, int64_t chunk, float* loss, float* lse, float* row_kl,
+                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+  kd::Plan p;
+  kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
+  if (st != KD_OK) return st;
+  st = check_forward_args(p, H, W, topk_idx, topk_logit, N, loss, lse, row_kl, workspace, workspace_bytes,
+                          p.bytes);
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (N == 0) {
+    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
+    return KD_OK;
+  }
+  return run_forward(p, H, W, topk_idx, topk_logit, N, D, V, K, T, loss, lse, row_kl,
+                     static_cast<char*>(workspace), nullptr, nullptr, s);
+}
+
+size_t kd_topk_kl_keep_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int64_t chunk) {
+  kd::KeepPlan kp;
+  if (kd::make_keep_plan(N, D, V, K, 1.f, chunk, &kp) != KD_OK) return 0;
+  return kp.bytes;
+}
+
+kd_status kd_topk_kl_forward_keep(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                  const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                                  float T, int64_t chunk, float* loss, float* lse, float* row_kl,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+  kd::KeepPlan kp;
+  kd_status st = kd::make_keep_plan(N, D, V, K, T, chunk, &kp);
+  if (st != KD_OK) return st;
+  st = check_forward_args(kp.base, H, W, topk_idx, topk_logit, N, loss, lse, row_kl, workspace,
+                          workspace_bytes, kp.bytes);
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (N == 0) {
+    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
+    return KD_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  return run_forward(kp.base, H, W, topk_idx, topk_logit, N, D, V, K, T, loss, lse, row_kl, ws,
+                     reinterpret_cast<float*>(ws + kp.off_z), reinterpret_cast<uint16_t*>(ws + kp.off_gall), s);
+}
+
+kd_status kd_topk_kl_backward_keep(const uint16_t* H, const uint16_t* W, const float* grad_loss,
+                                   int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                                   uint16_t* dH, float* dW, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream) {
+  kd::KeepPlan kp;
+  const kd_status st = kd::make_keep_plan(N, D, V, K, T, chunk, &kp);
+  if (st != KD_OK) return st;
+  const kd::Plan& p = kp.base;
+  if (bad_ptr(dW, 16)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(dH, 16))) return KD_ERR_INVALID_ARG;
+  if (grad_loss != nullptr && !kd::aligned(grad_loss, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (workspace == nullptr || workspace_bytes < kp.bytes)) return KD_ERR_WORKSPACE;
+  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
+  if (N == 0) return KD_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  const uint16_t* gall = reinterpret_cast<const uint16_t*>(ws + kp.off_gall);
+  float* dhp = reinterpret_cast<float*>(ws + kp.off_dhp);
+  const int ktiles = int(p.Vp / kd::gemm_bk());
+  const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
+  for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
+    const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
+    kd::DhArgs da{gall + row0 * p.Vp, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D,
+                  p.c_pad, grad_loss};
+    KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
+    if (p.dh_split > 1)
+      KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
+                kd::launch_dh_reduce(dhp, p.dh_split, rows, int(D), p.c_pad, dH + row0 * D, s));
+  }
+  for (int64_t r0 = 0; r0 < N; r0 += kp.dw_rows) {
+    const int rows = int(N - r0 < kp.dw_rows ? N - r0 : kp.dw_rows);
+    kd::DwArgs wa{gall + r0 * p.Vp, H + r0 * D, rows, int(D), int(V), p.Vp, dW, grad_loss};
+    KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
+  }
   return KD_OK;
 }
 

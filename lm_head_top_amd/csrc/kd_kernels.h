@@ -37,6 +37,7 @@ struct LogitsArgs {
   const int32_t* boff;
   const uint32_t* ent;
   // forward outputs
+  float* zkeep;         // [rows, Vp] fp32 z kept for the kept-gradient mode, or null
   float* pm;            // [nvt, c_pad] tile max of z
   float* ps;            // [nvt, c_pad] tile sum exp(z - max)
   float* zsel;          // [c_pad, K]   z at the cached ids
@@ -70,6 +71,7 @@ struct DhArgs {
   float* part;         // [split, c_pad, D] (split > 1)
   uint16_t* dH;        // [rows, D] offset to the chunk (split == 1)
   int64_t c_pad;
+  const float* scale;  // device scalar multiplying the result, or null
 };
 
 // dW += G^T H over a group of consecutive chunks (their G rows are stored
@@ -81,6 +83,7 @@ struct DwArgs {
   int D, V;
   int64_t Vp;
   float* dW;           // [V, D]
+  const float* scale;  // device scalar multiplying G^T H, or null
 };
 
 int gemm_bk();  // K depth of one GEMM pipeline stage
@@ -94,6 +97,10 @@ hipError_t launch_dh(const DhArgs& a, hipStream_t s);
 hipError_t launch_dh_reduce(const float* part, int split, int rows, int D, int64_t c_pad,
                             uint16_t* dH, hipStream_t s);
 hipError_t launch_dw(const DwArgs& a, hipStream_t s);
+// Kept-gradient mode: G_c = bf16(gs (exp(z - lse) - p scattered at the ids))
+// from the chunk's kept fp32 logits z [rows, Vp] (overwritten).
+hipError_t launch_keep_grad(float* z, const float* lse, const int32_t* idx, const float* p, int rows, int K,
+                            int V, int64_t Vp, float gs, uint16_t* G, hipStream_t s);
 hipError_t launch_validate(const int32_t* idx, int64_t N, int K, int64_t V, int32_t* flags,
                            hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);

@@ -528,7 +528,7 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
 
 // ----------------------------------------------------------- logits tile ---
 
-template <int MODE>  // 0: forward epilogue, 1: backward epilogue
+template <int MODE>  // 0: forward epilogue, 1: backward epilogue, 2: forward epilogue that also stores z
 KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   const int total = a.nvt * a.npt;
@@ -554,7 +554,7 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
   const int eend = a.boff[int64_t(pt) * (a.nvt + 1) + vt + 1];
   const uint32_t* ent = a.ent + int64_t(pt) * kTile * a.K;
 
-  if (MODE == 0) {
+  if (MODE == 0 || MODE == 2) {
     // z = acc / T; vocab rows past V do not exist
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -566,6 +566,23 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
           if (vtail && v0 + acc_row(wm, i, r, lane) >= a.V) z = -INFINITY;
           acc[i][j][r] = z;
         }
+    if (MODE == 2) {
+      // keep z[position][vocab] (fp32, row stride Vp): registers 4g .. 4g+3
+      // of a block are 4 consecutive vocab rows at one position
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int prow = p0 + acc_col(wn, j, lane);
+        if (prow < a.rows) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<float4*>(a.zkeep + int64_t(prow) * a.Vp + v0 + acc_row(wm, i, 4 * g, lane)) =
+                  make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                              acc[i][j][4 * g + 3]);
+        }
+      }
+    }
     // per-position max and sum of exp over the tile's 256 vocab rows
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -737,6 +754,7 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const float sc = a.scale != nullptr ? a.scale[0] : 1.f;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -747,9 +765,9 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
         const int prow = tm * kTile + acc_row(wm, i, r, lane);
         if (prow < a.rows && d < a.D) {
           if (a.split > 1)
-            a.part[(int64_t(sp) * a.c_pad + prow) * a.D + d] = acc[i][j][r];
+            a.part[(int64_t(sp) * a.c_pad + prow) * a.D + d] = sc * acc[i][j][r];
           else
-            a.dH[int64_t(prow) * a.D + d] = uint16_t(bf16_rne(acc[i][j][r]));
+            a.dH[int64_t(prow) * a.D + d] = uint16_t(bf16_rne(sc * acc[i][j][r]));
         }
       }
     }
@@ -792,6 +810,7 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const float sc = a.scale != nullptr ? a.scale[0] : 1.f;
   // dW += tile with one fp32 atomic add per element (no value returned): the
   // read-modify-write happens in L2, so the workgroup does not wait for the
   // old values.  Each element gets exactly one add per launch, so the result
@@ -804,9 +823,54 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = tm * kTile + acc_row(wm, i, r, lane);
-        if (v < a.V && d < a.D) unsafeAtomicAdd(a.dW + int64_t(v) * a.D + d, acc[i][j][r]);
+        if (v < a.V && d < a.D) unsafeAtomicAdd(a.dW + int64_t(v) * a.D + d, sc * acc[i][j][r]);
       }
     }
+}
+
+// ------------------------------------------------- kept-gradient (comparator) ---
+
+// z[p][v] <- exp(z[p][v] - lse[p]) in place, for p < rows, v < Vp (the kept
+// logits of one chunk; v >= V hold -inf and become 0).
+__global__ __launch_bounds__(NT) void keep_softmax_kernel(float* __restrict__ z, const float* __restrict__ lse,
+                                                          int rows, int64_t Vp) {
+  const int64_t q = int64_t(blockIdx.x) * NT + threadIdx.x;  // float4 index
+  const int64_t per_row = Vp / 4;
+  if (q >= int64_t(rows) * per_row) return;
+  const int64_t p = q / per_row;
+  const float l2 = lse[p] * LOG2E;
+  float4 v = reinterpret_cast<float4*>(z)[q];
+  v.x = exp2_fast(fmaf(v.x, LOG2E, -l2));
+  v.y = exp2_fast(fmaf(v.y, LOG2E, -l2));
+  v.z = exp2_fast(fmaf(v.z, LOG2E, -l2));
+  v.w = exp2_fast(fmaf(v.w, LOG2E, -l2));
+  reinterpret_cast<float4*>(z)[q] = v;
+}
+
+// z[p][idx[p][k]] -= p[p][k] (duplicates add up; ids outside [0, V) skipped).
+__global__ __launch_bounds__(NT) void keep_scatter_kernel(float* __restrict__ z, const int32_t* __restrict__ idx,
+                                                          const float* __restrict__ pk, int rows, int K, int V,
+                                                          int64_t Vp) {
+  const int64_t e = int64_t(blockIdx.x) * NT + threadIdx.x;
+  if (e >= int64_t(rows) * K) return;
+  const int64_t p = e / K;
+  const int id = idx[e];
+  if (unsigned(id) < unsigned(V)) atomicAdd(z + p * Vp + id, -pk[e]);
+}
+
+// G[p][v] = bf16(gs * z[p][v]) for p < rows, v < Vp (16 bytes of G per thread).
+__global__ __launch_bounds__(NT) void keep_convert_kernel(const float* __restrict__ z, float gs, int rows,
+                                                          int64_t Vp, uint16_t* __restrict__ G) {
+  const int64_t q = int64_t(blockIdx.x) * NT + threadIdx.x;  // 8-element index
+  if (q >= int64_t(rows) * (Vp / 8)) return;
+  const float4 x0 = reinterpret_cast<const float4*>(z)[2 * q];
+  const float4 x1 = reinterpret_cast<const float4*>(z)[2 * q + 1];
+  uint4 o;
+  o.x = bf16_rne(gs * x0.x) | (bf16_rne(gs * x0.y) << 16);
+  o.y = bf16_rne(gs * x0.z) | (bf16_rne(gs * x0.w) << 16);
+  o.z = bf16_rne(gs * x1.x) | (bf16_rne(gs * x1.y) << 16);
+  o.w = bf16_rne(gs * x1.z) | (bf16_rne(gs * x1.w) << 16);
+  reinterpret_cast<uint4*>(G)[q] = o;
 }
 
 // ---------------------------------------------------------------- utility ---
@@ -852,7 +916,26 @@ hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s) {
 }
 
 hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(logits_kernel<0>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+  if (a.zkeep != nullptr)
+    hipLaunchKernelGGL(logits_kernel<2>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+  else
+    hipLaunchKernelGGL(logits_kernel<0>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_keep_grad(float* z, const float* lse, const int32_t* idx, const float* p, int rows, int K,
+                            int V, int64_t Vp, float gs, uint16_t* G, hipStream_t s) {
+  const int64_t n4 = int64_t(rows) * (Vp / 4);
+  hipLaunchKernelGGL(keep_softmax_kernel, dim3(unsigned(ceil_div(n4, NT))), dim3(NT), 0, s, z, lse, rows, Vp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ne = int64_t(rows) * K;
+  hipLaunchKernelGGL(keep_scatter_kernel, dim3(unsigned(ceil_div(ne, NT))), dim3(NT), 0, s, z, idx, p, rows, K,
+                     V, Vp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n8 = int64_t(rows) * (Vp / 8);
+  hipLaunchKernelGGL(keep_convert_kernel, dim3(unsigned(ceil_div(n8, NT))), dim3(NT), 0, s, z, gs, rows, Vp, G);
   return hipGetLastError();
 }
 

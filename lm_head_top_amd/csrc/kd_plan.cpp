@@ -101,4 +101,33 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
   return KD_OK;
 }
 
+kd_status make_keep_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                         KeepPlan* plan) {
+  if (plan == nullptr) return KD_ERR_INVALID_ARG;
+  KeepPlan kp;
+  const kd_status st = make_plan(N, D, V, K, T, chunk, &kp.base);
+  if (st != KD_OK) return st;
+  const Plan& p = kp.base;
+  // the forward-only region ends at off_rowkl + N * 4; everything kept goes after it
+  size_t off = align_up(p.off_rowkl + size_t(N > 0 ? N : 1) * 4);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  kp.off_z = take(size_t(p.chunk) * p.Vp * 4);
+  kp.off_gall = take(size_t(N > 0 ? N : 1) * p.Vp * 2);
+  kp.off_dhp = take(p.dh_split > 1 ? size_t(p.dh_split) * p.c_pad * D * 4 : 0);
+  kp.bytes = off;
+  // rows per dW GEMM: G and H are addressed with 32-bit offsets from the group's first row
+  const int64_t lim = (int64_t(1) << 31) - 64;
+  int64_t L = lim / (p.Vp * 2);
+  if (lim / (D * 2) < L) L = lim / (D * 2);
+  L = L / kTile * kTile;
+  if (L < kTile) return KD_ERR_UNSUPPORTED;
+  kp.dw_rows = N < L ? (N > 0 ? N : 1) : L;
+  *plan = kp;
+  return KD_OK;
+}
+
 }  // namespace kd

@@ -33,6 +33,18 @@ struct Plan {
   size_t bytes = 0;
 };
 
+// Kept-gradient mode (the comparator that keeps G for the backward instead of
+// recomputing it): the forward region of the plan, the chunk's fp32 logits,
+// G for all N positions (bf16 [N, Vp]) and the dH split partials.
+struct KeepPlan {
+  Plan base;
+  size_t off_z = 0, off_gall = 0, off_dhp = 0, bytes = 0;
+  int64_t dw_rows = 0;  // positions per dW GEMM (32-bit buffer offsets into G and H)
+};
+
+kd_status make_keep_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                         KeepPlan* plan);
+
 // Fills `plan` from the problem sizes.  Returns KD_OK or the reason the sizes
 // are rejected.  Does not look at pointers.
 kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,

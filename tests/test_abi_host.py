@@ -158,10 +158,10 @@ def test_validate_rejects(lib):
 def test_profile_api(lib):
     ms = ctypes.c_double()
     n = ctypes.c_int64()
-    assert lib.kd_profile_enable(1 << 10) == KD_ERR_INVALID_ARG
+    assert lib.kd_profile_enable(1 << 11) == KD_ERR_INVALID_ARG
     assert lib.kd_profile_read(-1, ctypes.byref(ms), ctypes.byref(n)) == KD_ERR_INVALID_ARG
     assert lib.kd_profile_enable(0) == KD_OK
-    assert lib.kd_profile_enable(0x3FF) == KD_OK
+    assert lib.kd_profile_enable(0x7FF) == KD_OK
     assert lib.kd_profile_enable(0) == KD_OK
     assert lib.kd_profile_read(1, ctypes.byref(ms), ctypes.byref(n)) == KD_OK
     assert n.value == 0 and ms.value == 0.0
@@ -207,3 +207,28 @@ def test_topk_select_rejects(lib):
     assert f(vp(2), 0, 4, 100, 10, ok, ok, None) == KD_ERR_INVALID_ARG   # fp32 needs 4-byte alignment
     assert f(None, 1, 4, 100, 10, ok, ok, None) == KD_ERR_INVALID_ARG    # null logits
     assert f(None, 0, 0, 100, 10, None, None, None) == KD_OK             # empty: nothing to do
+
+
+def test_keep_workspace_is_order_N_times_V(lib):
+    """The kept-gradient comparator holds G for every position: its workspace
+    grows by about 2 V bytes per position (bf16 G), unlike the fused one."""
+    f = kd.keep_workspace_size
+    a = f(8192, 4096, 131072, 100, 1024)
+    b = f(16384, 4096, 131072, 100, 1024)
+    per_pos = (b - a) / 8192
+    assert 2 * 131072 <= per_pos <= 2 * 131072 + 16
+    assert a > kd.workspace_size(8192, 4096, 131072, 100, 1024)
+    assert f(-1, 8, 8, 1, 1) == 0
+
+
+def test_keep_entry_points_reject(lib):
+    vp = ctypes.c_void_p
+    ok = vp(256)
+    assert lib.kd_topk_kl_backward_keep(ok, ok, None, 16, 8, 64, 4, 1.0, 8, ok, ok, ok, 16,
+                                        None) == KD_ERR_WORKSPACE
+    assert lib.kd_topk_kl_backward_keep(ok, ok, None, 16, 8, 64, 4, 1.0, 8, ok, vp(4), ok, 1 << 30,
+                                        None) == KD_ERR_INVALID_ARG  # dW misaligned
+    assert lib.kd_topk_kl_forward_keep(ok, ok, ok, ok, 16, 8, 64, 4, 1.0, 8, ok, ok, None, ok, 16,
+                                       None) == KD_ERR_WORKSPACE
+    assert lib.kd_topk_kl_forward_keep(ok, ok, ok, ok, 16, 7, 64, 4, 1.0, 8, ok, ok, None, ok, 1 << 30,
+                                       None) == KD_ERR_INVALID_ARG  # D % 8
