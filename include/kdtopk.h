@@ -154,6 +154,37 @@ kd_status kd_topk_kl_backward_keep(const uint16_t* H, const uint16_t* W, const f
                                    void* hip_stream);
 
 /*
+ * Dense-teacher (online) mode: the same fused loss with the teacher's full-
+ * vocabulary logits streamed chunk by chunk instead of a top-K cache, i.e.
+ * KL(softmax(t/T) || softmax(z/T)) over all V entries (the online
+ * distillation setup the cache replaces: "Distilling an LLM on One GPU",
+ * section "Why distillation recovery is expensive"; "Breaking the Memory
+ * Barrier", section "Detailed Chronology and Technical Evolution").
+ *
+ *   teacher_logits  [N, V], t_dtype KD_DTYPE_F32 (16-byte aligned) or
+ *                   KD_DTYPE_BF16 (8-byte aligned); V % 4 == 0
+ *   lse, lse_t      fp32 [N] out (forward) / in (backward): student and
+ *                   teacher log-normalisers at temperature T
+ *   loss, row_kl, dH, dW, grad_loss, workspace   as in the top-K entry points
+ *                   (workspace: kd_dense_kl_workspace_size bytes)
+ *
+ *   KL_n = sum_v p (a - z/T) - lse_t + lse,  a = t/T,  p = softmax(a);
+ *   G = g/(N T) (softmax(z/T) - softmax(t/T)).
+ * A row whose teacher logits are all -inf is outside the contract.  The
+ * teacher logits are read once in the forward and once in the backward.
+ */
+size_t kd_dense_kl_workspace_size(int64_t N, int64_t D, int64_t V, int64_t chunk);
+kd_status kd_dense_kl_forward(const uint16_t* H, const uint16_t* W, const void* teacher_logits,
+                              int32_t t_dtype, int64_t N, int64_t D, int64_t V, float T, int64_t chunk,
+                              float* loss, float* lse, float* lse_t, float* row_kl, void* workspace,
+                              size_t workspace_bytes, void* hip_stream);
+kd_status kd_dense_kl_backward(const uint16_t* H, const uint16_t* W, const void* teacher_logits,
+                               int32_t t_dtype, const float* lse, const float* lse_t,
+                               const float* grad_loss, int64_t N, int64_t D, int64_t V, float T,
+                               int64_t chunk, uint16_t* dH, float* dW, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
+
+/*
  * Debug aid, not on the hot path: checks the teacher cache's ids.
  * d_flags (device int32 [1]) is overwritten with bit 0 set if some id lies
  * outside [0, V) and bit 1 set if some row holds an id twice.

@@ -16,6 +16,7 @@ __all__ = [
     "lib_path", "load_library", "workspace_size", "forward", "backward", "validate",
     "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError", "topk_select",
     "keep_workspace_size", "forward_keep", "backward_keep",
+    "dense_workspace_size", "dense_forward", "dense_backward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,14 @@ def load_library():
     lib.kd_topk_kl_backward_keep.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_f, c_i64,
                                              c_vp, c_vp, c_vp, c_sz, c_vp]
     lib.kd_topk_kl_backward_keep.restype = ctypes.c_int
+    lib.kd_dense_kl_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64]
+    lib.kd_dense_kl_workspace_size.restype = c_sz
+    lib.kd_dense_kl_forward.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_f, c_i64,
+                                        c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+    lib.kd_dense_kl_forward.restype = ctypes.c_int
+    lib.kd_dense_kl_backward.argtypes = [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
+                                         c_f, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]
+    lib.kd_dense_kl_backward.restype = ctypes.c_int
     lib.kd_topk_select.argtypes = [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]
     lib.kd_topk_select.restype = ctypes.c_int
     lib.kd_last_hip_error.argtypes = []
@@ -226,6 +235,67 @@ def backward_keep(H, W, K: int, workspace, grad_loss=None, T: float = 1.0, chunk
         _ptr(H), _ptr(W), _ptr(gl), N, D, V, int(K), float(T), int(chunk), _ptr(dH), _ptr(dW),
         _ptr(workspace), workspace.numel(), _stream_ptr(torch, dev))
     _check(st, "kd_topk_kl_backward_keep")
+    return dH, dW
+
+
+def _teacher_dtype(torch, teacher):
+    if teacher.dtype == torch.float32:
+        return 0
+    if teacher.dtype == torch.bfloat16:
+        return 1
+    raise TypeError("teacher logits must be float32 or bfloat16")
+
+
+def dense_workspace_size(N: int, D: int, V: int, chunk: int) -> int:
+    return int(load_library().kd_dense_kl_workspace_size(N, D, V, chunk))
+
+
+def _dense_workspace(torch, N, D, V, chunk, device, workspace):
+    need = dense_workspace_size(N, D, V, chunk)
+    if need == 0:
+        raise KDError(1, "dense_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def dense_forward(H, W, teacher, T: float = 1.0, chunk: int = 1024, want_row_kl: bool = False,
+                  workspace=None):
+    """Dense-teacher KL over the full vocabulary: loss, lse, lse_t [, row_kl]."""
+    torch = _torch()
+    N, D = H.shape
+    V = W.shape[0]
+    if tuple(teacher.shape) != (N, V) or not teacher.is_contiguous() or not teacher.is_cuda:
+        raise ValueError("teacher logits must be a contiguous device tensor [N, V]")
+    dev = H.device
+    ws = _dense_workspace(torch, N, D, V, chunk, dev, workspace)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    lse_t = torch.empty(N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(N, dtype=torch.float32, device=dev) if want_row_kl else None
+    st = load_library().kd_dense_kl_forward(
+        _ptr(H), _ptr(W), _ptr(teacher), _teacher_dtype(torch, teacher), N, D, V, float(T), int(chunk),
+        _ptr(loss), _ptr(lse), _ptr(lse_t), _ptr(row_kl), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
+    _check(st, "kd_dense_kl_forward")
+    return (loss, lse, lse_t, row_kl) if want_row_kl else (loss, lse, lse_t)
+
+
+def dense_backward(H, W, teacher, lse, lse_t, grad_loss=None, T: float = 1.0, chunk: int = 1024,
+                   dW=None, workspace=None):
+    """dH (overwritten) and dW (accumulated) of the dense-teacher KL."""
+    torch = _torch()
+    N, D = H.shape
+    V = W.shape[0]
+    dev = H.device
+    ws = _dense_workspace(torch, N, D, V, chunk, dev, workspace)
+    dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    if dW is None:
+        dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
+    gl = grad_loss.contiguous() if grad_loss is not None else None
+    st = load_library().kd_dense_kl_backward(
+        _ptr(H), _ptr(W), _ptr(teacher), _teacher_dtype(torch, teacher), _ptr(lse), _ptr(lse_t), _ptr(gl),
+        N, D, V, float(T), int(chunk), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
+    _check(st, "kd_dense_kl_backward")
     return dH, dW
 
 

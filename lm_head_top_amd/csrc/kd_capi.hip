@@ -141,6 +141,82 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
   return KD_OK;
 }
 
+// The backward's chunk loop: recompute each chunk's logits, form G_c (top-K
+// cache, or a dense teacher when tlog is set), dH_c = G_c W, and every
+// dw_group chunks dW += G^T H.
+kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                       const float* topk_logit, const void* tlog, int t_dtype, const float* lse,
+                       const float* lse_t, const float* grad_loss, int64_t N, int64_t D, int64_t V,
+                       int32_t K, float T, uint16_t* dH, float* dW, char* ws, hipStream_t s) {
+  float* pw = reinterpret_cast<float*>(ws + p.off_p);
+  float* hw = reinterpret_cast<float*>(ws + p.off_h);
+  int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
+  uint32_t* ent = reinterpret_cast<uint32_t*>(ws + p.off_ent);
+  uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
+  float* dhp = reinterpret_cast<float*>(ws + p.off_dhp);
+  const float invT = 1.f / T;
+  const float g_scale = float(1.0 / (double(N) * double(T)));
+  const int ktiles = int(p.Vp / kd::gemm_bk());
+  const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
+  const size_t esz = t_dtype == KD_DTYPE_F32 ? 4 : 2;
+
+  // The G rows of up to dw_group consecutive chunks are kept one after
+  // another (position order, row stride Vp) and feed one dW GEMM with K = the
+  // group's positions; H rows of the group are consecutive in H already.
+  int gj = 0;
+  int64_t group_row0 = 0;
+  for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
+    const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
+    const int npt = (rows + kd::kTile - 1) / kd::kTile;
+    if (gj == 0) group_row0 = row0;
+    uint16_t* Gc = G + (row0 - group_row0) * p.Vp;
+    kd::LogitsArgs la{};
+    if (tlog == nullptr) {
+      kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
+      KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
+      kd::BucketArgs ba{topk_idx + row0 * K, rows, K, int(V), int(p.nvt), boff, ent};
+      KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, npt, s));
+      la.boff = boff;
+      la.ent = ent;
+      la.p = pw;
+    } else {
+      la.tlog = static_cast<const char*>(tlog) + row0 * V * esz;
+      la.t_dtype = t_dtype;
+      la.lse_t = lse_t + row0;
+    }
+    la.W = W;
+    la.Hc = H + row0 * D;
+    la.rows = rows;
+    la.D = int(D);
+    la.V = int(V);
+    la.K = K;
+    la.nvt = int(p.nvt);
+    la.npt = npt;
+    la.c_pad = p.c_pad;
+    la.Vp = p.Vp;
+    la.invT = invT;
+    la.lse = lse + row0;
+    la.grad_loss = grad_loss;
+    la.g_scale = g_scale;
+    la.G = Gc;
+    KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
+    kd::DhArgs da{Gc, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
+    KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
+    if (p.dh_split > 1)
+      KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
+                kd::launch_dh_reduce(dhp, p.dh_split, rows, int(D), p.c_pad, dH + row0 * D, s));
+    ++gj;
+    const bool last = row0 + p.chunk >= N;
+    if (gj == p.dw_group || last) {
+      const int grows = int(row0 + rows - group_row0);
+      kd::DwArgs wa{G, H + group_row0 * D, grows, int(D), int(V), p.Vp, dW};
+      KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
+      gj = 0;
+    }
+  }
+  return KD_OK;
+}
+
 kd_status check_forward_args(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
                              const float* topk_logit, int64_t N, float* loss, float* lse, float* row_kl,
                              void* workspace, size_t workspace_bytes, size_t need) {
@@ -257,68 +333,94 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
   if (N > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return KD_ERR_WORKSPACE;
   if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
   if (N == 0) return KD_OK;  // nothing to accumulate
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  char* ws = static_cast<char*>(workspace);
-  float* pw = reinterpret_cast<float*>(ws + p.off_p);
-  float* hw = reinterpret_cast<float*>(ws + p.off_h);
-  int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
-  uint32_t* ent = reinterpret_cast<uint32_t*>(ws + p.off_ent);
-  uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
-  float* dhp = reinterpret_cast<float*>(ws + p.off_dhp);
-  const float invT = 1.f / T;
-  const float g_scale = float(1.0 / (double(N) * double(T)));
-  const int ktiles = int(p.Vp / kd::gemm_bk());
-  const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
+  return run_backward(p, H, W, topk_idx, topk_logit, nullptr, 0, lse, nullptr, grad_loss, N, D, V, K, T,
+                      dH, dW, static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream));
+}
 
-  // The G rows of up to dw_group consecutive chunks are kept one after
-  // another (position order, row stride Vp) and feed one dW GEMM with K = the
-  // group's positions; H rows of the group are consecutive in H already.
-  int gj = 0;
-  int64_t group_row0 = 0;
+size_t kd_dense_kl_workspace_size(int64_t N, int64_t D, int64_t V, int64_t chunk) {
+  kd::DensePlan dp;
+  if (kd::make_dense_plan(N, D, V, 1.f, chunk, &dp) != KD_OK) return 0;
+  return dp.bytes;
+}
+
+kd_status kd_dense_kl_forward(const uint16_t* H, const uint16_t* W, const void* teacher_logits,
+                              int32_t t_dtype, int64_t N, int64_t D, int64_t V, float T, int64_t chunk,
+                              float* loss, float* lse, float* lse_t, float* row_kl, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+  kd::DensePlan dp;
+  kd_status st = kd::make_dense_plan(N, D, V, T, chunk, &dp);
+  if (st != KD_OK) return st;
+  if (t_dtype != KD_DTYPE_F32 && t_dtype != KD_DTYPE_BF16) return KD_ERR_INVALID_ARG;
+  if (bad_ptr(loss, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(lse, 4) || bad_ptr(lse_t, 4) ||
+                bad_ptr(teacher_logits, t_dtype == KD_DTYPE_F32 ? 16 : 8)))
+    return KD_ERR_INVALID_ARG;
+  if (row_kl != nullptr && !kd::aligned(row_kl, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (workspace == nullptr || workspace_bytes < dp.bytes)) return KD_ERR_WORKSPACE;
+  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (N == 0) {
+    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
+    return KD_OK;
+  }
+  const kd::Plan& p = dp.base;
+  char* ws = static_cast<char*>(workspace);
+  float* pm = reinterpret_cast<float*>(ws + p.off_pm);
+  float* ps = reinterpret_cast<float*>(ws + p.off_ps);
+  float* tm = reinterpret_cast<float*>(ws + dp.off_tm);
+  float* ts0 = reinterpret_cast<float*>(ws + dp.off_ts0);
+  float* ts1 = reinterpret_cast<float*>(ws + dp.off_ts1);
+  float* rowkl = row_kl != nullptr ? row_kl : reinterpret_cast<float*>(ws + p.off_rowkl);
+  const size_t esz = t_dtype == KD_DTYPE_F32 ? 4 : 2;
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
     const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
-    const int npt = (rows + kd::kTile - 1) / kd::kTile;
-    if (gj == 0) group_row0 = row0;
-    uint16_t* Gc = G + (row0 - group_row0) * p.Vp;
-    kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
-    KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
-    kd::BucketArgs ba{topk_idx + row0 * K, rows, K, int(V), int(p.nvt), boff, ent};
-    KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, npt, s));
     kd::LogitsArgs la{};
     la.W = W;
     la.Hc = H + row0 * D;
     la.rows = rows;
     la.D = int(D);
     la.V = int(V);
-    la.K = K;
+    la.K = 1;
     la.nvt = int(p.nvt);
-    la.npt = npt;
+    la.npt = (rows + kd::kTile - 1) / kd::kTile;
     la.c_pad = p.c_pad;
     la.Vp = p.Vp;
-    la.invT = invT;
-    la.boff = boff;
-    la.ent = ent;
-    la.lse = lse + row0;
-    la.p = pw;
-    la.grad_loss = grad_loss;
-    la.g_scale = g_scale;
-    la.G = Gc;
-    KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
-    kd::DhArgs da{Gc, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
-    KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
-    if (p.dh_split > 1)
-      KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
-                kd::launch_dh_reduce(dhp, p.dh_split, rows, int(D), p.c_pad, dH + row0 * D, s));
-    ++gj;
-    const bool last = row0 + p.chunk >= N;
-    if (gj == p.dw_group || last) {
-      const int grows = int(row0 + rows - group_row0);
-      kd::DwArgs wa{G, H + group_row0 * D, grows, int(D), int(V), p.Vp, dW};
-      KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
-      gj = 0;
-    }
+    la.invT = 1.f / T;
+    la.tlog = static_cast<const char*>(teacher_logits) + row0 * V * esz;
+    la.t_dtype = t_dtype;
+    la.tm = tm;
+    la.ts0 = ts0;
+    la.ts1 = ts1;
+    la.pm = pm;
+    la.ps = ps;
+    KD_LAUNCH(KD_KERNEL_LOGITS_FWD, s, kd::launch_logits_fwd(la, s));
+    kd::DenseCombineArgs ca{pm, ps, tm, ts0, ts1, rows, int(p.nvt), p.c_pad, lse + row0, lse_t + row0,
+                            rowkl + row0};
+    KD_LAUNCH(KD_KERNEL_COMBINE, s, kd::launch_dense_combine(ca, s));
   }
+  KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, N, loss, s));
   return KD_OK;
+}
+
+kd_status kd_dense_kl_backward(const uint16_t* H, const uint16_t* W, const void* teacher_logits,
+                               int32_t t_dtype, const float* lse, const float* lse_t,
+                               const float* grad_loss, int64_t N, int64_t D, int64_t V, float T,
+                               int64_t chunk, uint16_t* dH, float* dW, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  kd::DensePlan dp;
+  const kd_status st = kd::make_dense_plan(N, D, V, T, chunk, &dp);
+  if (st != KD_OK) return st;
+  if (t_dtype != KD_DTYPE_F32 && t_dtype != KD_DTYPE_BF16) return KD_ERR_INVALID_ARG;
+  if (bad_ptr(dW, 16)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(lse, 4) || bad_ptr(lse_t, 4) ||
+                bad_ptr(dH, 16) || bad_ptr(teacher_logits, t_dtype == KD_DTYPE_F32 ? 16 : 8)))
+    return KD_ERR_INVALID_ARG;
+  if (grad_loss != nullptr && !kd::aligned(grad_loss, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (workspace == nullptr || workspace_bytes < dp.bytes)) return KD_ERR_WORKSPACE;
+  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
+  if (N == 0) return KD_OK;
+  return run_backward(dp.base, H, W, nullptr, nullptr, teacher_logits, t_dtype, lse, lse_t, grad_loss, N, D,
+                      V, 1, T, dH, dW, static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream));
 }
 
 kd_status kd_topk_kl_validate(const int32_t* topk_idx, int64_t N, int32_t K, int64_t V,

@@ -36,6 +36,13 @@ struct LogitsArgs {
   float invT;
   const int32_t* boff;
   const uint32_t* ent;
+  // dense teacher (full-vocabulary teacher logits instead of the top-K cache)
+  const void* tlog;     // [rows, V] teacher logits of the chunk (fp32 or bf16), or null
+  int t_dtype;          // 0 fp32, 1 bf16
+  float* tm;            // [nvt, c_pad] tile max of t / T
+  float* ts0;           // [nvt, c_pad] tile sum exp(a - max)
+  float* ts1;           // [nvt, c_pad] tile sum exp(a - max) (a - z)
+  const float* lse_t;   // [rows] teacher log-normaliser (backward)
   // forward outputs
   float* zkeep;         // [rows, Vp] fp32 z kept for the kept-gradient mode, or null
   float* pm;            // [nvt, c_pad] tile max of z
@@ -47,6 +54,19 @@ struct LogitsArgs {
   const float* grad_loss;  // device scalar or null
   float g_scale;        // 1 / (N T)
   uint16_t* G;          // [rows, Vp] bf16, offset to the chunk's first row (zero past V)
+};
+
+struct DenseCombineArgs {
+  const float* pm;
+  const float* ps;
+  const float* tm;
+  const float* ts0;
+  const float* ts1;
+  int rows, nvt;
+  int64_t c_pad;
+  float* lse;      // [rows], offset to the chunk
+  float* lse_t;    // [rows], offset to the chunk
+  float* rowkl;    // [rows], offset to the chunk
 };
 
 struct CombineArgs {
@@ -93,6 +113,7 @@ hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_finalize(const float* rowkl, int64_t N, float* loss, hipStream_t s);
+hipError_t launch_dense_combine(const DenseCombineArgs& a, hipStream_t s);
 hipError_t launch_dh(const DhArgs& a, hipStream_t s);
 hipError_t launch_dh_reduce(const float* part, int split, int rows, int D, int64_t c_pad,
                             uint16_t* dH, hipStream_t s);

@@ -82,7 +82,7 @@ constexpr int NS = BK / 16;                      // 16-deep MFMA steps per stage
 constexpr int LPS = KD_LPS;                      // ring loads issued per MFMA step (front-loaded)
 constexpr int SLD = kTile + 4;                   // fp32 row stride of the epilogue staging tile
 constexpr int STAGE_FLOATS = 128 * SLD;          // half a tile: 128 positions x 256 vocab
-constexpr int EPI_BYTES = (STAGE_FLOATS + 4 * kTile) * 4;
+constexpr int EPI_BYTES = (STAGE_FLOATS + 10 * kTile) * 4;
 constexpr int SMEM_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
 constexpr uint32_t kOOB = 0xFFFFFFF0u;           // buffer offset past any operand: reads return 0
 constexpr float LOG2E = 1.4426950408889634f;
@@ -528,7 +528,37 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
 
 // ----------------------------------------------------------- logits tile ---
 
-template <int MODE>  // 0: forward epilogue, 1: backward epilogue, 2: forward epilogue that also stores z
+// (m, S0, S1) <- merge of two teacher triples (max of a, sum exp(a - max),
+// sum exp(a - max) (a - b)).
+__device__ __forceinline__ void tri_merge(float& m, float& s0, float& s1, float m2, float t0, float t1) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) {
+    m = M;
+    s0 = s1 = 0.f;
+    return;
+  }
+  const float e1 = exp2_fast((m - M) * LOG2E), e2 = exp2_fast((m2 - M) * LOG2E);
+  s0 = s0 * e1 + t0 * e2;
+  s1 = s1 * e1 + t1 * e2;
+  m = M;
+}
+
+// Four consecutive teacher logits t[p][v .. v+3] (fp32 or bf16), times 1/T.
+__device__ __forceinline__ float4 teacher4(const void* t, int dtype, int64_t off, float invT) {
+  float4 x;
+  if (dtype == 0) {
+    x = *reinterpret_cast<const float4*>(static_cast<const float*>(t) + off);
+  } else {
+    const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(t) + off);
+    x = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
+                    __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
+  }
+  return make_float4(x.x * invT, x.y * invT, x.z * invT, x.w * invT);
+}
+
+// 0: forward epilogue, 1: backward epilogue, 2: forward epilogue that also
+// stores z, 3: dense-teacher forward epilogue, 4: dense-teacher backward epilogue
+template <int MODE>
 KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   const int total = a.nvt * a.npt;
@@ -550,11 +580,12 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
   float* S = reinterpret_cast<float*>(smem);
   float* red = S + STAGE_FLOATS;  // [4][256]
   const bool vtail = v0 + kTile > a.V;
-  const int ebeg = a.boff[int64_t(pt) * (a.nvt + 1) + vt];
-  const int eend = a.boff[int64_t(pt) * (a.nvt + 1) + vt + 1];
-  const uint32_t* ent = a.ent + int64_t(pt) * kTile * a.K;
+  constexpr bool CACHE = MODE <= 2;  // top-K cache entries (the dense-teacher modes have none)
+  const int ebeg = CACHE ? a.boff[int64_t(pt) * (a.nvt + 1) + vt] : 0;
+  const int eend = CACHE ? a.boff[int64_t(pt) * (a.nvt + 1) + vt + 1] : 0;
+  const uint32_t* ent = CACHE ? a.ent + int64_t(pt) * kTile * a.K : nullptr;
 
-  if (MODE == 0 || MODE == 2) {
+  if (MODE == 0 || MODE == 2 || MODE == 3) {
     // z = acc / T; vocab rows past V do not exist
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -606,6 +637,46 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
         red[(2 + wm) * kTile + pl] = s;
       }
     }
+    if (MODE == 3) {
+      // teacher: a = t / T over the same (vocab, position) tile; per position
+      // max of a, sum exp(a - max) and sum exp(a - max) (a - z)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int pl = acc_col(wn, j, lane);
+        const bool prow_ok = p0 + pl < a.rows;
+        float tm = -INFINITY, t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int vr = v0 + acc_row(wm, i, 4 * g, lane);
+            if (!prow_ok || vr >= a.V) continue;
+            const float4 t4 = teacher4(a.tlog, a.t_dtype, int64_t(p0 + pl) * a.V + vr, a.invT);
+            const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+            float m4 = fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3]));
+            if (m4 > tm) {
+              const float sc = tm == -INFINITY ? 0.f : exp2_fast((tm - m4) * LOG2E);
+              t0 *= sc;
+              t1 *= sc;
+              tm = m4;
+            }
+            if (tm == -INFINITY) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (tv[q] == -INFINITY) continue;
+              const float e = exp2_fast((tv[q] - tm) * LOG2E);
+              t0 += e;
+              t1 += e * (tv[q] - acc[i][j][4 * g + q]);
+            }
+          }
+        tri_merge(tm, t0, t1, __shfl_xor(tm, 32), __shfl_xor(t0, 32), __shfl_xor(t1, 32));
+        if (lane < 32) {
+          red[(4 + wm) * kTile + pl] = tm;
+          red[(6 + wm) * kTile + pl] = t0;
+          red[(8 + wm) * kTile + pl] = t1;
+        }
+      }
+    }
     __syncthreads();
     if (tid < kTile) {
       float m = red[tid], s = red[2 * kTile + tid];
@@ -615,8 +686,17 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
         a.pm[int64_t(vt) * a.c_pad + prow] = m;
         a.ps[int64_t(vt) * a.c_pad + prow] = s;
       }
+      if (MODE == 3) {
+        float tm = red[4 * kTile + tid], t0 = red[6 * kTile + tid], t1 = red[8 * kTile + tid];
+        tri_merge(tm, t0, t1, red[5 * kTile + tid], red[7 * kTile + tid], red[9 * kTile + tid]);
+        if (prow < a.rows) {
+          a.tm[int64_t(vt) * a.c_pad + prow] = tm;
+          a.ts0[int64_t(vt) * a.c_pad + prow] = t0;
+          a.ts1[int64_t(vt) * a.c_pad + prow] = t1;
+        }
+      }
     }
-    if (ebeg == eend) return;
+    if (MODE == 3 || ebeg == eend) return;
     // logits at the cached ids that fall in this tile
     for (int h = 0; h < 2; ++h) {
       stage_half(S, acc, wm, wn, lane, h);
@@ -650,6 +730,27 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
           if (vtail && v0 + acc_row(wm, i, r, lane) >= a.V) q = 0.f;
           acc[i][j][r] = gs * q;
         }
+    if (MODE == 4) {
+      // minus gs * softmax(t / T) over the full vocabulary, from the teacher's lse
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int pl = acc_col(wn, j, lane);
+        if (p0 + pl >= a.rows) continue;
+        const float tl2 = a.lse_t[p0 + pl] * LOG2E;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int vr = v0 + acc_row(wm, i, 4 * g, lane);
+            if (vr >= a.V) continue;
+            const float4 t4 = teacher4(a.tlog, a.t_dtype, int64_t(p0 + pl) * a.V + vr, a.invT);
+            acc[i][j][4 * g] -= gs * exp2_fast(fmaf(t4.x, LOG2E, -tl2));
+            acc[i][j][4 * g + 1] -= gs * exp2_fast(fmaf(t4.y, LOG2E, -tl2));
+            acc[i][j][4 * g + 2] -= gs * exp2_fast(fmaf(t4.z, LOG2E, -tl2));
+            acc[i][j][4 * g + 3] -= gs * exp2_fast(fmaf(t4.w, LOG2E, -tl2));
+          }
+      }
+    }
     for (int h = 0; h < 2; ++h) {
       stage_half(S, acc, wm, wn, lane, h);
       __syncthreads();
@@ -714,6 +815,25 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   }
 }
 
+// Dense teacher: lse of the student and of the teacher from the vocab-tile
+// partials, and KL_n = sum_v p (a - z) - lse_a + lse_z with
+// sum_v p (a - z) = S1 / S0.
+__global__ __launch_bounds__(NT) void dense_combine_kernel(DenseCombineArgs a) {
+  const int r = blockIdx.x * NT + threadIdx.x;
+  if (r >= a.rows) return;
+  float m = -INFINITY, s = 0.f, tm = -INFINITY, t0 = 0.f, t1 = 0.f;
+  for (int vt = 0; vt < a.nvt; ++vt) {
+    const int64_t o = int64_t(vt) * a.c_pad + r;
+    lse_merge(m, s, a.pm[o], a.ps[o]);
+    tri_merge(tm, t0, t1, a.tm[o], a.ts0[o], a.ts1[o]);
+  }
+  const float lse = m + logf(s);
+  const float lse_t = tm + logf(t0);
+  a.lse[r] = lse;
+  a.lse_t[r] = lse_t;
+  a.rowkl[r] = t1 / t0 - lse_t + lse;
+}
+
 __global__ __launch_bounds__(NT) void finalize_kernel(const float* __restrict__ rowkl, int64_t N,
                                                       float* __restrict__ loss) {
   __shared__ double red[NT];
@@ -754,7 +874,9 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const float sc = a.scale != nullptr ? a.scale[0] : 1.f;
+  // uniform: one scalar register, so later stores never wait on its load
+  const float sc = a.scale != nullptr ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.scale[0])))
+                                      : 1.f;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -810,7 +932,9 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const float sc = a.scale != nullptr ? a.scale[0] : 1.f;
+  // uniform: one scalar register, so later stores never wait on its load
+  const float sc = a.scale != nullptr ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.scale[0])))
+                                      : 1.f;
   // dW += tile with one fp32 atomic add per element (no value returned): the
   // read-modify-write happens in L2, so the workgroup does not wait for the
   // old values.  Each element gets exactly one add per launch, so the result
@@ -916,7 +1040,9 @@ hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s) {
 }
 
 hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s) {
-  if (a.zkeep != nullptr)
+  if (a.tlog != nullptr)
+    hipLaunchKernelGGL(logits_kernel<3>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+  else if (a.zkeep != nullptr)
     hipLaunchKernelGGL(logits_kernel<2>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
   else
     hipLaunchKernelGGL(logits_kernel<0>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
@@ -940,12 +1066,20 @@ hipError_t launch_keep_grad(float* z, const float* lse, const int32_t* idx, cons
 }
 
 hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(logits_kernel<1>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+  if (a.tlog != nullptr)
+    hipLaunchKernelGGL(logits_kernel<4>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+  else
+    hipLaunchKernelGGL(logits_kernel<1>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned(ceil_div(a.rows, 32))), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_combine(const DenseCombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(dense_combine_kernel, dim3(unsigned(ceil_div(a.rows, NT))), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

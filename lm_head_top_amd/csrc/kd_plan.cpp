@@ -130,4 +130,26 @@ kd_status make_keep_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, in
   return KD_OK;
 }
 
+kd_status make_dense_plan(int64_t N, int64_t D, int64_t V, float T, int64_t chunk, DensePlan* plan) {
+  if (plan == nullptr) return KD_ERR_INVALID_ARG;
+  if (V % 4 != 0) return KD_ERR_INVALID_ARG;  // the teacher is read 4 logits at a time
+  DensePlan dp;
+  const kd_status st = make_plan(N, D, V, 1, T, chunk, &dp.base);
+  if (st != KD_OK) return st;
+  const Plan& p = dp.base;
+  size_t off = align_up(p.bytes);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t part = size_t(p.nvt) * p.c_pad * 4;
+  dp.off_tm = take(part);
+  dp.off_ts0 = take(part);
+  dp.off_ts1 = take(part);
+  dp.bytes = off;
+  *plan = dp;
+  return KD_OK;
+}
+
 }  // namespace kd

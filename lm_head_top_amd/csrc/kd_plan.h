@@ -45,6 +45,16 @@ struct KeepPlan {
 kd_status make_keep_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
                          KeepPlan* plan);
 
+// Dense-teacher mode (full-vocabulary teacher logits streamed per chunk
+// instead of a top-K cache): the plan of the top-K path with K = 1 (its cache
+// buffers go unused) plus the teacher's per-tile partials.
+struct DensePlan {
+  Plan base;
+  size_t off_tm = 0, off_ts0 = 0, off_ts1 = 0, bytes = 0;
+};
+
+kd_status make_dense_plan(int64_t N, int64_t D, int64_t V, float T, int64_t chunk, DensePlan* plan);
+
 // Fills `plan` from the problem sizes.  Returns KD_OK or the reason the sizes
 // are rejected.  Does not look at pointers.
 kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,

@@ -232,3 +232,18 @@ def test_keep_entry_points_reject(lib):
                                        None) == KD_ERR_WORKSPACE
     assert lib.kd_topk_kl_forward_keep(ok, ok, ok, ok, 16, 7, 64, 4, 1.0, 8, ok, ok, None, ok, 1 << 30,
                                        None) == KD_ERR_INVALID_ARG  # D % 8
+
+
+def test_dense_entry_points_reject(lib):
+    vp = ctypes.c_void_p
+    ok = vp(256)
+    assert kd.dense_workspace_size(8192, 4096, 131070, 1024) == 0          # V % 4 != 0
+    assert kd.dense_workspace_size(8192, 4096, 131072, 1024) > 0
+    f = lib.kd_dense_kl_forward
+    assert f(ok, ok, ok, 2, 16, 8, 64, 1.0, 8, ok, ok, ok, None, ok, 1 << 30, None) == KD_ERR_INVALID_ARG
+    assert f(ok, ok, vp(264), 0, 16, 8, 64, 1.0, 8, ok, ok, ok, None, ok, 1 << 30,
+             None) == KD_ERR_INVALID_ARG                                    # fp32 teacher not 16-byte aligned
+    assert f(ok, ok, ok, 0, 16, 8, 64, 1.0, 8, ok, ok, ok, None, ok, 16, None) == KD_ERR_WORKSPACE
+    b = lib.kd_dense_kl_backward
+    assert b(ok, ok, ok, 0, ok, ok, None, 16, 8, 64, 1.0, 8, ok, vp(8), ok, 1 << 30,
+             None) == KD_ERR_INVALID_ARG                                    # dW misaligned
