@@ -424,6 +424,117 @@ def keep_compare(args):
     print(json.dumps(line), flush=True)
 
 
+def loss_ext(args):
+    """The loss extensions on --config beside the plain loss, same inputs: a
+    0/1 position mask (about 10% of positions masked, as padding would), a
+    hard label per position (about 5% without one) mixed in with weights
+    0.5 / 0.5, and T^2 scaling.  Time of one forward + backward each."""
+    import torch
+    import lm_head_top_amd as kd
+    from synth import get_config
+    kd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    N, D, V, K, T, chunk = cfg.N, cfg.D, cfg.V, cfg.K, cfg.T, cfg.chunk
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    W = (torch.randn((V, D), generator=g, device=dev) * D ** -0.5).to(torch.bfloat16)
+    H, idx, t = _gpu_inputs(torch, N, D, V, K, args.seed + 1, dev)
+    mask = (torch.rand(N, generator=g, device=dev) >= 0.1).float()
+    labels = torch.randint(0, V, (N,), generator=g, device=dev, dtype=torch.int32)
+    labels[torch.rand(N, generator=g, device=dev) < 0.05] = -1
+    dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kd.workspace_size(N, D, V, K, chunk), dtype=torch.uint8, device=dev)
+    ext = dict(row_weight=mask, labels=labels, kd_weight=0.5, ce_weight=0.5, scale_T2=True)
+
+    def plain():
+        loss, lse = kd.forward(H, W, idx, t, T, chunk, workspace=ws)
+        kd.backward(H, W, idx, t, lse, None, T, chunk, dW=dW, workspace=ws)
+        return loss
+
+    def extended():
+        loss, lse = kd.forward_ex(H, W, idx, t, T, chunk, workspace=ws, **ext)
+        kd.backward_ex(H, W, idx, t, lse, None, T, chunk, dW=dW, workspace=ws, **ext)
+        return loss
+
+    out = {}
+    for name, fn in (("plain", plain), ("extended", extended)):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(args.steps, 1)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            loss = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        out[name] = {"ms_median": round(times[len(times) // 2], 3), "loss": float(loss.item()),
+                     "tokens_per_s": round(N / (times[len(times) // 2] * 1e-3), 1)}
+        log(f"{name}: {out[name]}")
+    line = {"mode": "loss_extensions", "config": {**_config_doc(cfg, args.seed),
+                                                  "mask_frac": 0.1, "no_label_frac": 0.05,
+                                                  "kd_weight": 0.5, "ce_weight": 0.5, "scale_T2": True},
+            **out, "time_ratio_extended_over_plain":
+                round(out["extended"]["ms_median"] / out["plain"]["ms_median"], 4)}
+    print(json.dumps(line), flush=True)
+
+
+def dense_teacher(args):
+    """Dense-teacher (online) mode on --config: the student's fused forward +
+    backward against full-vocabulary teacher logits (fp32 or bf16, drawn on the
+    device from a seeded generator).  Reports tokens/s and the extra HBM
+    stream of teacher logits (read once per pass)."""
+    import numpy as np
+    import torch
+    import lm_head_top_amd as kd
+    from synth import get_config, make_inputs
+    kd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    inp = make_inputs(cfg, args.seed)
+    H = torch.from_numpy(inp["H"].view(np.int16)).view(torch.bfloat16).to(dev)
+    W = torch.from_numpy(inp["W"].view(np.int16)).view(torch.bfloat16).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed + 1)
+    tt = torch.randn((cfg.N, cfg.V), generator=g, device=dev) * 3 ** 0.5
+    if args.topk_dtype == "bf16":
+        tt = tt.to(torch.bfloat16)
+    ws = torch.empty(kd.dense_workspace_size(cfg.N, cfg.D, cfg.V, cfg.chunk), dtype=torch.uint8,
+                     device=dev)
+    dW = torch.zeros((cfg.V, cfg.D), dtype=torch.float32, device=dev)
+
+    def step():
+        loss, lse, lse_t = kd.dense_forward(H, W, tt, cfg.T, cfg.chunk, workspace=ws)
+        kd.dense_backward(H, W, tt, lse, lse_t, None, cfg.T, cfg.chunk, dW=dW, workspace=ws)
+        return loss
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        loss = step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = 8.0 * cfg.N * cfg.D * cfg.V / (ms * 1e-3) / 1e12
+    line = {"mode": "dense_teacher", "metric": "fused dense-teacher KL fwd+bwd tokens/s", "unit": "tokens/s",
+            "value": round(cfg.N / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "steps": args.steps,
+            "tflops": round(tflops, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+            "teacher_dtype": args.topk_dtype,
+            "teacher_bytes_per_step": 2 * cfg.N * cfg.V * tt.element_size(),
+            "peak_hbm_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
+            "loss": float(loss.item()), "config": _config_doc(cfg, args.seed)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,15 +569,25 @@ def main():
     ap.add_argument("--topk-dtype", default="f32", choices=("f32", "bf16"))
     ap.add_argument("--keep-compare", action="store_true",
                     help="the fused loss beside the kept-gradient comparator on --config")
+    ap.add_argument("--dense-teacher", action="store_true",
+                    help="the dense-teacher (full-vocabulary) mode on --config "
+                         "(teacher dtype from --topk-dtype)")
+    ap.add_argument("--loss-ext", action="store_true",
+                    help="the loss extensions (mask, hard-label mix, T^2) beside the plain loss "
+                         "on --config")
     args = ap.parse_args()
-    if args.keep_compare:
-        if args.gpus != 1:
-            sys.exit(2)
-        keep_compare(args)
+    if args.gpus != 1 and not (args.stats_from or args.traffic_from):
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the loss runs on one "
+              "device, and how it would shard over several is described, not implemented",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.loss_ext:
+        loss_ext(args)
+        return
+    if args.keep_compare or args.dense_teacher:
+        (keep_compare if args.keep_compare else dense_teacher)(args)
         return
     if args.memory_sweep or args.dense_reference or args.topk_writer:
-        if args.gpus != 1:
-            sys.exit(2)
         if args.memory_sweep:
             memory_sweep(args)
         elif args.dense_reference:
@@ -489,10 +610,6 @@ def main():
         write_traffic(args.traffic_from[0], args.traffic_from[1], args.copy_calibration_mib,
                       args.traffic_command, _config_doc(get_config(args.config), args.seed))
         return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the method's "
-              "multi-GPU sharding is a design note, not part of this build", file=sys.stderr)
-        sys.exit(2)
 
     import numpy as np
     import torch

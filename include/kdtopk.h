@@ -126,6 +126,42 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W,
                               void* hip_stream);
 
 /*
+ * Loss extensions (the pages report ablations over loss terms and a cost of
+ * packing sequences with an all-ones mask: "The $250GB Memory Spike That
+ * Killed Distillation Projects Is Now Optional", section "What a Single H200
+ * GPU Can Now Do That Once Required Four Nodes").  With z, lse, p and KL_n as
+ * above:
+ *
+ *   CE_n   = lse_n - z[n, y_n]  for a label 0 <= y_n < V, else 0
+ *   l_n    = s (kd_weight KL_n + ce_weight CE_n),  s = T^2 with KD_SCALE_T2, else 1
+ *   loss   = sum_n w_n l_n / sum_n w_n   (w_n = 1 without row_weight; 0 if the
+ *                                         weights sum to 0)
+ *   G[n,v] = g s (w_n / sum w) / T ((kd_weight + ce_weight [label]) softmax(z_n)_v
+ *            - kd_weight sum_{k: idx=v} p[n,k] - ce_weight [v = y_n])
+ *
+ *   row_weight  fp32 [N] or NULL (a 0/1 mask, or any finite weights)
+ *   labels      int32 [N] or NULL (no cross-entropy term); y_n outside [0, V)
+ *               means no label for that position
+ *   flags       0 or KD_SCALE_T2
+ *   row_loss    fp32 [N] out or NULL: l_n
+ * Everything else as in kd_topk_kl_forward / kd_topk_kl_backward (same
+ * workspace size).  The plain entry points are the case row_weight = labels =
+ * NULL, kd_weight = 1, flags = 0.
+ */
+enum { KD_SCALE_T2 = 1 };
+kd_status kd_topk_kl_forward_ex(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                                float T, int64_t chunk, const float* row_weight, const int32_t* labels,
+                                float kd_weight, float ce_weight, int32_t flags, float* loss, float* lse,
+                                float* row_loss, void* workspace, size_t workspace_bytes, void* hip_stream);
+kd_status kd_topk_kl_backward_ex(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                 const float* topk_logit, const float* lse, const float* grad_loss,
+                                 int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                                 const float* row_weight, const int32_t* labels, float kd_weight,
+                                 float ce_weight, int32_t flags, uint16_t* dH, float* dW, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+
+/*
  * Kept-gradient comparator (the "forward-chunked" variant the pages compare
  * against: it keeps what the backward needs instead of recomputing it; "The
  * $250GB Memory Spike That Killed Distillation Projects Is Now Optional",

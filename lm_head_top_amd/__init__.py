@@ -16,7 +16,7 @@ __all__ = [
     "lib_path", "load_library", "workspace_size", "forward", "backward", "validate",
     "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError", "topk_select",
     "keep_workspace_size", "forward_keep", "backward_keep",
-    "dense_workspace_size", "dense_forward", "dense_backward",
+    "dense_workspace_size", "dense_forward", "dense_backward", "forward_ex", "backward_ex",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +70,13 @@ def load_library():
     lib.kd_topk_kl_backward.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                         c_i32, c_f, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]
     lib.kd_topk_kl_backward.restype = ctypes.c_int
+    lib.kd_topk_kl_forward_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_f, c_i64,
+                                          c_vp, c_vp, c_f, c_f, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+    lib.kd_topk_kl_forward_ex.restype = ctypes.c_int
+    lib.kd_topk_kl_backward_ex.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32,
+                                           c_f, c_i64, c_vp, c_vp, c_f, c_f, c_i32, c_vp, c_vp, c_vp, c_sz,
+                                           c_vp]
+    lib.kd_topk_kl_backward_ex.restype = ctypes.c_int
     lib.kd_topk_kl_validate.argtypes = [c_vp, c_i64, c_i32, c_i64, c_vp, c_vp]
     lib.kd_topk_kl_validate.restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
@@ -189,6 +196,67 @@ def backward(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0,
         _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), _ptr(lse), _ptr(gl), N, D, V, K,
         float(T), int(chunk), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
     _check(st, "kd_topk_kl_backward")
+    return dH, dW
+
+
+KD_SCALE_T2 = 1
+
+
+def _ext_args(torch, N, row_weight, labels):
+    if row_weight is not None and (row_weight.dtype != torch.float32 or row_weight.numel() != N
+                                   or not row_weight.is_contiguous() or not row_weight.is_cuda):
+        raise ValueError("row_weight must be a contiguous float32 device tensor [N]")
+    if labels is not None and (labels.dtype != torch.int32 or labels.numel() != N
+                               or not labels.is_contiguous() or not labels.is_cuda):
+        raise ValueError("labels must be a contiguous int32 device tensor [N]")
+
+
+def forward_ex(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024, row_weight=None,
+               labels=None, kd_weight: float = 1.0, ce_weight: float = 0.0, scale_T2: bool = False,
+               want_row_loss: bool = False, workspace=None):
+    """Loss with the extensions: per-position weights, a hard-label
+    cross-entropy term and T^2 scaling.  Returns loss, lse [, row_loss]."""
+    torch = _torch()
+    N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
+    _ext_args(torch, N, row_weight, labels)
+    dev = H.device
+    ws = _workspace(torch, N, D, V, K, chunk, dev, workspace)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(N, dtype=torch.float32, device=dev) if want_row_loss else None
+    st = load_library().kd_topk_kl_forward_ex(
+        _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), N, D, V, K, float(T), int(chunk),
+        _ptr(row_weight), _ptr(labels), float(kd_weight), float(ce_weight),
+        KD_SCALE_T2 if scale_T2 else 0, _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(ws), ws.numel(),
+        _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_forward_ex")
+    return (loss, lse, row_loss) if want_row_loss else (loss, lse)
+
+
+def backward_ex(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0, chunk: int = 1024,
+                row_weight=None, labels=None, kd_weight: float = 1.0, ce_weight: float = 0.0,
+                scale_T2: bool = False, dW=None, workspace=None):
+    """dH (overwritten) and dW (accumulated) of the extended loss."""
+    torch = _torch()
+    N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
+    _ext_args(torch, N, row_weight, labels)
+    dev = H.device
+    if lse.dtype != torch.float32 or lse.numel() != N or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [N]")
+    if grad_loss is not None and (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1):
+        raise ValueError("grad_loss must be a float32 device scalar")
+    ws = _workspace(torch, N, D, V, K, chunk, dev, workspace)
+    dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    if dW is None:
+        dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
+    elif dW.dtype != torch.float32 or tuple(dW.shape) != (V, D) or not dW.is_contiguous():
+        raise ValueError("dW must be a contiguous float32 [V, D] tensor")
+    gl = grad_loss.contiguous() if grad_loss is not None else None
+    st = load_library().kd_topk_kl_backward_ex(
+        _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), _ptr(lse), _ptr(gl), N, D, V, K,
+        float(T), int(chunk), _ptr(row_weight), _ptr(labels), float(kd_weight), float(ce_weight),
+        KD_SCALE_T2 if scale_T2 else 0, _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_backward_ex")
     return dH, dW
 
 

@@ -2,6 +2,7 @@
 // and kernel launches on the caller's stream.  Declared in include/kdtopk.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 #include <vector>
 
@@ -87,12 +88,20 @@ size_t kd_topk_kl_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int
 
 namespace {
 
+// Loss extensions: per-position weights, hard labels mixed in with weight
+// beta beside the KL term's alpha, and an overall factor (T^2 or 1).
+struct LossExt {
+  const float* row_w = nullptr;
+  const int32_t* labels = nullptr;
+  float alpha = 1.f, beta = 0.f, scale = 1.f;
+};
+
 // The forward's chunk loop.  With zkeep / gall set (kept-gradient mode) each
 // chunk's fp32 logits are kept and turned into its G rows of gall.
 kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
                       const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K, float T,
                       float* loss, float* lse, float* row_kl, char* ws, float* zkeep, uint16_t* gall,
-                      hipStream_t s) {
+                      hipStream_t s, const LossExt& ext = LossExt()) {
   float* pw = reinterpret_cast<float*>(ws + p.off_p);
   float* hw = reinterpret_cast<float*>(ws + p.off_h);
   int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
@@ -109,9 +118,20 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
     const int npt = (rows + kd::kTile - 1) / kd::kTile;
     kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
     KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
-    kd::BucketArgs ba{topk_idx + row0 * K, rows, K, int(V), int(p.nvt), boff, ent};
+    const int KE = K + (ext.labels != nullptr ? 1 : 0);
+    kd::BucketArgs ba{};
+    ba.idx = topk_idx + row0 * K;
+    ba.rows = rows;
+    ba.K = K;
+    ba.V = int(V);
+    ba.nvt = int(p.nvt);
+    ba.KE = KE;
+    ba.labels = ext.labels != nullptr ? ext.labels + row0 : nullptr;
+    ba.boff = boff;
+    ba.ent = ent;
     KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, npt, s));
     kd::LogitsArgs la{};
+    la.KE = KE;
     la.W = W;
     la.Hc = H + row0 * D;
     la.rows = rows;
@@ -130,14 +150,31 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
     la.ps = ps;
     la.zsel = zsel;
     KD_LAUNCH(KD_KERNEL_LOGITS_FWD, s, kd::launch_logits_fwd(la, s));
-    kd::CombineArgs ca{pm, ps, zsel, pw, hw, rows, K, int(p.nvt), p.c_pad, lse + row0, rowkl + row0};
+    kd::CombineArgs ca{};
+    ca.pm = pm;
+    ca.ps = ps;
+    ca.zsel = zsel;
+    ca.p = pw;
+    ca.h = hw;
+    ca.rows = rows;
+    ca.K = K;
+    ca.nvt = int(p.nvt);
+    ca.KE = KE;
+    ca.V = int(V);
+    ca.labels = ext.labels != nullptr ? ext.labels + row0 : nullptr;
+    ca.alpha = ext.alpha;
+    ca.beta = ext.beta;
+    ca.scale = ext.scale;
+    ca.c_pad = p.c_pad;
+    ca.lse = lse + row0;
+    ca.rowkl = rowkl + row0;
     KD_LAUNCH(KD_KERNEL_COMBINE, s, kd::launch_combine(ca, s));
     if (zkeep != nullptr)
       KD_LAUNCH(KD_KERNEL_KEEP_GRAD, s,
                 kd::launch_keep_grad(zkeep, lse + row0, topk_idx + row0 * K, pw, rows, K, int(V), p.Vp,
                                      g_scale, gall + row0 * p.Vp, s));
   }
-  KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, N, loss, s));
+  KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, ext.row_w, N, loss, nullptr, s));
   return KD_OK;
 }
 
@@ -147,18 +184,25 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
 kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
                        const float* topk_logit, const void* tlog, int t_dtype, const float* lse,
                        const float* lse_t, const float* grad_loss, int64_t N, int64_t D, int64_t V,
-                       int32_t K, float T, uint16_t* dH, float* dW, char* ws, hipStream_t s) {
+                       int32_t K, float T, uint16_t* dH, float* dW, char* ws, hipStream_t s,
+                       const LossExt& ext = LossExt()) {
   float* pw = reinterpret_cast<float*>(ws + p.off_p);
   float* hw = reinterpret_cast<float*>(ws + p.off_h);
   int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
   uint32_t* ent = reinterpret_cast<uint32_t*>(ws + p.off_ent);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
   float* dhp = reinterpret_cast<float*>(ws + p.off_dhp);
+  float* inv_wsum = reinterpret_cast<float*>(ws + p.off_scalar);
   const float invT = 1.f / T;
-  const float g_scale = float(1.0 / (double(N) * double(T)));
+  // the per-row factor is 1/N without weights, w_n / sum w with them
+  const float g_scale = ext.row_w != nullptr ? float(double(ext.scale) / double(T))
+                                             : float(double(ext.scale) / (double(N) * double(T)));
   const int ktiles = int(p.Vp / kd::gemm_bk());
   const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
   const size_t esz = t_dtype == KD_DTYPE_F32 ? 4 : 2;
+  if (ext.row_w != nullptr)
+    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(nullptr, ext.row_w, N, nullptr, inv_wsum, s));
+  const int KE = K + (ext.labels != nullptr ? 1 : 0);
 
   // The G rows of up to dw_group consecutive chunks are kept one after
   // another (position order, row stride Vp) and feed one dW GEMM with K = the
@@ -174,7 +218,16 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
     if (tlog == nullptr) {
       kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
       KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
-      kd::BucketArgs ba{topk_idx + row0 * K, rows, K, int(V), int(p.nvt), boff, ent};
+      kd::BucketArgs ba{};
+      ba.idx = topk_idx + row0 * K;
+      ba.rows = rows;
+      ba.K = K;
+      ba.V = int(V);
+      ba.nvt = int(p.nvt);
+      ba.KE = KE;
+      ba.labels = ext.labels != nullptr ? ext.labels + row0 : nullptr;
+      ba.boff = boff;
+      ba.ent = ent;
       KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, npt, s));
       la.boff = boff;
       la.ent = ent;
@@ -198,6 +251,12 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
     la.lse = lse + row0;
     la.grad_loss = grad_loss;
     la.g_scale = g_scale;
+    la.KE = KE;
+    la.row_w = ext.row_w != nullptr ? ext.row_w + row0 : nullptr;
+    la.inv_wsum = inv_wsum;
+    la.labels = ext.labels != nullptr ? ext.labels + row0 : nullptr;
+    la.alpha = ext.alpha;
+    la.beta = ext.beta;
     la.G = Gc;
     KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
     kd::DhArgs da{Gc, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
@@ -337,6 +396,68 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
                       dH, dW, static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream));
 }
 
+kd_status kd_topk_kl_forward_ex(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                                float T, int64_t chunk, const float* row_weight, const int32_t* labels,
+                                float kd_weight, float ce_weight, int32_t flags, float* loss, float* lse,
+                                float* row_loss, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  kd::Plan p;
+  kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
+  if (st != KD_OK) return st;
+  if ((flags & ~KD_SCALE_T2) != 0 || !std::isfinite(kd_weight) || !std::isfinite(ce_weight))
+    return KD_ERR_INVALID_ARG;
+  if (N > 0 && ((row_weight != nullptr && !kd::aligned(row_weight, 4)) ||
+                (labels != nullptr && !kd::aligned(labels, 4))))
+    return KD_ERR_INVALID_ARG;
+  st = check_forward_args(p, H, W, topk_idx, topk_logit, N, loss, lse, row_loss, workspace, workspace_bytes,
+                          p.bytes);
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (N == 0) {
+    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
+    return KD_OK;
+  }
+  LossExt ext;
+  ext.row_w = row_weight;
+  ext.labels = labels;
+  ext.alpha = kd_weight;
+  ext.beta = labels != nullptr ? ce_weight : 0.f;
+  ext.scale = (flags & KD_SCALE_T2) ? T * T : 1.f;
+  return run_forward(p, H, W, topk_idx, topk_logit, N, D, V, K, T, loss, lse, row_loss,
+                     static_cast<char*>(workspace), nullptr, nullptr, s, ext);
+}
+
+kd_status kd_topk_kl_backward_ex(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                 const float* topk_logit, const float* lse, const float* grad_loss,
+                                 int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                                 const float* row_weight, const int32_t* labels, float kd_weight,
+                                 float ce_weight, int32_t flags, uint16_t* dH, float* dW, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+  kd::Plan p;
+  const kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
+  if (st != KD_OK) return st;
+  if ((flags & ~KD_SCALE_T2) != 0 || !std::isfinite(kd_weight) || !std::isfinite(ce_weight))
+    return KD_ERR_INVALID_ARG;
+  if (bad_ptr(dW, 16)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(topk_idx, 4) ||
+                bad_ptr(topk_logit, 4) || bad_ptr(lse, 4) || bad_ptr(dH, 16) ||
+                (row_weight != nullptr && !kd::aligned(row_weight, 4)) ||
+                (labels != nullptr && !kd::aligned(labels, 4))))
+    return KD_ERR_INVALID_ARG;
+  if (grad_loss != nullptr && !kd::aligned(grad_loss, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return KD_ERR_WORKSPACE;
+  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
+  if (N == 0) return KD_OK;
+  LossExt ext;
+  ext.row_w = row_weight;
+  ext.labels = labels;
+  ext.alpha = kd_weight;
+  ext.beta = labels != nullptr ? ce_weight : 0.f;
+  ext.scale = (flags & KD_SCALE_T2) ? T * T : 1.f;
+  return run_backward(p, H, W, topk_idx, topk_logit, nullptr, 0, lse, nullptr, grad_loss, N, D, V, K, T, dH,
+                      dW, static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream), ext);
+}
+
 size_t kd_dense_kl_workspace_size(int64_t N, int64_t D, int64_t V, int64_t chunk) {
   kd::DensePlan dp;
   if (kd::make_dense_plan(N, D, V, 1.f, chunk, &dp) != KD_OK) return 0;
@@ -398,7 +519,7 @@ kd_status kd_dense_kl_forward(const uint16_t* H, const uint16_t* W, const void* 
                             rowkl + row0};
     KD_LAUNCH(KD_KERNEL_COMBINE, s, kd::launch_dense_combine(ca, s));
   }
-  KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, N, loss, s));
+  KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, nullptr, N, loss, nullptr, s));
   return KD_OK;
 }
 

@@ -22,6 +22,8 @@ struct TeacherArgs {
 struct BucketArgs {
   const int32_t* idx;   // [rows, K], offset to the chunk's first row
   int rows, K, V, nvt;
+  int KE;               // entries per row: K, or K + 1 with labels
+  const int32_t* labels;  // [rows] hard labels (offset to the chunk), or null
   int32_t* boff;        // [npt, nvt + 1]
   uint32_t* ent;        // [npt, kTile * K]
 };
@@ -36,6 +38,7 @@ struct LogitsArgs {
   float invT;
   const int32_t* boff;
   const uint32_t* ent;
+  int KE;               // cache entries per row (K, or K + 1 with the label last)
   // dense teacher (full-vocabulary teacher logits instead of the top-K cache)
   const void* tlog;     // [rows, V] teacher logits of the chunk (fp32 or bf16), or null
   int t_dtype;          // 0 fp32, 1 bf16
@@ -52,7 +55,12 @@ struct LogitsArgs {
   const float* lse;     // [rows] offset to the chunk
   const float* p;       // [c_pad, K]
   const float* grad_loss;  // device scalar or null
-  float g_scale;        // 1 / (N T)
+  float g_scale;        // s / (N T) without row weights, s / T with them (s = T^2 or 1)
+  // loss extensions (defaults: no weights, no labels, alpha 1, beta 0)
+  const float* row_w;     // [rows] per-position weights, offset to the chunk, or null
+  const float* inv_wsum;  // device scalar 1 / sum of all weights (with row_w)
+  const int32_t* labels;  // [rows] hard labels, offset to the chunk, or null
+  float alpha, beta;      // weights of the KL and the cross-entropy terms
   uint16_t* G;          // [rows, Vp] bf16, offset to the chunk's first row (zero past V)
 };
 
@@ -72,10 +80,13 @@ struct DenseCombineArgs {
 struct CombineArgs {
   const float* pm;
   const float* ps;
-  const float* zsel;
+  const float* zsel;    // [c_pad, KE]
   const float* p;
   const float* h;
   int rows, K, nvt;
+  int KE, V;
+  const int32_t* labels;  // [rows] offset to the chunk, or null
+  float alpha, beta, scale;
   int64_t c_pad;
   float* lse;      // [rows], offset to the chunk
   float* rowkl;    // [rows], offset to the chunk
@@ -112,7 +123,8 @@ hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s);
 hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
-hipError_t launch_finalize(const float* rowkl, int64_t N, float* loss, hipStream_t s);
+hipError_t launch_finalize(const float* rowl, const float* w, int64_t N, float* loss, float* inv_wsum,
+                           hipStream_t s);
 hipError_t launch_dense_combine(const DenseCombineArgs& a, hipStream_t s);
 hipError_t launch_dh(const DhArgs& a, hipStream_t s);
 hipError_t launch_dh_reduce(const float* part, int split, int rows, int D, int64_t c_pad,

@@ -455,18 +455,25 @@ __global__ __launch_bounds__(NT) void teacher_kernel(TeacherArgs a) {
   if (lane == 0) a.h[row] = hs;
 }
 
-// Counting sort of one position tile's cache entries by vocab tile.  Entry
-// word: row-in-tile << 16 | id % 256 << 8 | k.  Ids outside [0, V) are dropped.
+// Counting sort of one position tile's cache entries by vocab tile.  A row
+// has KE entries: its K cached ids (k < K) and, with labels, the label (k =
+// K).  Entry word: row-in-tile << 17 | id % 256 << 9 | k.  Ids outside
+// [0, V) (and negative labels) are dropped.
 constexpr int BT = 1024;  // threads of the bucketing kernel
+__device__ __forceinline__ int entry_id(const BucketArgs& a, const int32_t* idx, int r0, int e) {
+  const int rr = e / a.KE, k = e - rr * a.KE;
+  return k < a.K ? idx[int64_t(rr) * a.K + k] : a.labels[r0 + rr];
+}
+
 __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   __shared__ int cnt[kMaxVocabTiles];
   __shared__ int part[BT];
   const int pt = blockIdx.x, tid = threadIdx.x;
   const int r0 = pt * kTile;
   const int nr = min(kTile, a.rows - r0);
-  const int K = a.K, nvt = a.nvt;
-  const int ne = nr * K;
-  const int32_t* idx = a.idx + int64_t(r0) * K;
+  const int nvt = a.nvt;
+  const int ne = nr * a.KE;
+  const int32_t* idx = a.idx + int64_t(r0) * a.K;
   for (int v = tid; v < nvt; v += BT) cnt[v] = 0;
   __syncthreads();
   for (int e0 = 0; e0 < ne; e0 += 4 * BT) {
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + u * BT + tid;
-      id[u] = e < ne ? idx[e] : -1;
+      id[u] = e < ne ? entry_id(a, idx, r0, e) : -1;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -507,21 +514,21 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   }
   if (tid == BT - 1) bo[nvt] = part[BT - 1];
   __syncthreads();
-  uint32_t* ent = a.ent + int64_t(pt) * kTile * K;
+  uint32_t* ent = a.ent + int64_t(pt) * kTile * a.KE;
   for (int e0 = 0; e0 < ne; e0 += 4 * BT) {
     int id[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + u * BT + tid;
-      id[u] = e < ne ? idx[e] : -1;
+      id[u] = e < ne ? entry_id(a, idx, r0, e) : -1;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (unsigned(id[u]) < unsigned(a.V)) {
         const int e = e0 + u * BT + tid;
-        const int rr = e / K, k = e - rr * K;
+        const int rr = e / a.KE, k = e - rr * a.KE;
         const int pos = atomicAdd(&cnt[id[u] >> 8], 1);
-        ent[pos] = (uint32_t(rr) << 16) | (uint32_t(id[u] & (kTile - 1)) << 8) | uint32_t(k);
+        ent[pos] = (uint32_t(rr) << 17) | (uint32_t(id[u] & (kTile - 1)) << 9) | uint32_t(k);
       }
   }
 }
@@ -583,7 +590,7 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
   constexpr bool CACHE = MODE <= 2;  // top-K cache entries (the dense-teacher modes have none)
   const int ebeg = CACHE ? a.boff[int64_t(pt) * (a.nvt + 1) + vt] : 0;
   const int eend = CACHE ? a.boff[int64_t(pt) * (a.nvt + 1) + vt + 1] : 0;
-  const uint32_t* ent = CACHE ? a.ent + int64_t(pt) * kTile * a.K : nullptr;
+  const uint32_t* ent = CACHE ? a.ent + int64_t(pt) * kTile * a.KE : nullptr;
 
   if (MODE == 0 || MODE == 2 || MODE == 3) {
     // z = acc / T; vocab rows past V do not exist
@@ -703,21 +710,27 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
       __syncthreads();
       for (int e = ebeg + tid; e < eend; e += GT) {
         const uint32_t pk = ent[e];
-        const int row = int(pk >> 16);
+        const int row = int(pk >> 17);
         if ((row >> 7) == h) {
-          const int vl = int((pk >> 8) & 0xffu), k = int(pk & 0xffu);
-          a.zsel[int64_t(p0 + row) * a.K + k] = S[(row & 127) * SLD + vl];
+          const int vl = int((pk >> 9) & 0xffu), k = int(pk & 0x1ffu);
+          a.zsel[int64_t(p0 + row) * a.KE + k] = S[(row & 127) * SLD + vl];
         }
       }
       __syncthreads();
     }
   } else {
     const float gs = a.g_scale * (a.grad_loss != nullptr ? a.grad_loss[0] : 1.f);
-    float lse_l2[NJ];
+    const float iws = a.row_w != nullptr ? a.inv_wsum[0] : 1.f;
+    // per position: lse, and gs * w_n / sum w * (alpha + beta [label]) on the softmax
+    float lse_l2[NJ], qs[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int prow = p0 + acc_col(wn, j, lane);
-      lse_l2[j] = prow < a.rows ? a.lse[prow] * LOG2E : INFINITY;
+      const bool ok = prow < a.rows;
+      lse_l2[j] = ok ? a.lse[prow] * LOG2E : INFINITY;
+      const float rs = ok && a.row_w != nullptr ? a.row_w[prow] * iws : 1.f;
+      const bool lab = ok && a.labels != nullptr && unsigned(a.labels[prow]) < unsigned(a.V);
+      qs[j] = gs * rs * (lab ? a.alpha + a.beta : a.alpha);
     }
     // gs * softmax(z) over the full vocabulary, from the forward's lse
 #pragma unroll
@@ -728,7 +741,7 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
         for (int r = 0; r < 16; ++r) {
           float q = exp2_fast(fmaf(acc[i][j][r] * a.invT, LOG2E, -lse_l2[j]));
           if (vtail && v0 + acc_row(wm, i, r, lane) >= a.V) q = 0.f;
-          acc[i][j][r] = gs * q;
+          acc[i][j][r] = qs[j] * q;
         }
     if (MODE == 4) {
       // minus gs * softmax(t / T) over the full vocabulary, from the teacher's lse
@@ -754,13 +767,17 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
     for (int h = 0; h < 2; ++h) {
       stage_half(S, acc, wm, wn, lane, h);
       __syncthreads();
-      // minus the teacher probability at each cached id (scatter-add)
+      // minus alpha p at each cached id and beta at the label (scatter-add),
+      // times gs w_n / sum w
       for (int e = ebeg + tid; e < eend; e += GT) {
         const uint32_t pk = ent[e];
-        const int row = int(pk >> 16);
+        const int row = int(pk >> 17);
         if ((row >> 7) == h) {
-          const int vl = int((pk >> 8) & 0xffu), k = int(pk & 0xffu);
-          atomicAdd(S + (row & 127) * SLD + vl, -gs * a.p[int64_t(p0 + row) * a.K + k]);
+          const int vl = int((pk >> 9) & 0xffu), k = int(pk & 0x1ffu);
+          const int prow = p0 + row;
+          const float rs = a.row_w != nullptr ? a.row_w[prow] * iws : 1.f;
+          const float mass = k < a.K ? a.alpha * a.p[int64_t(prow) * a.K + k] : a.beta;
+          atomicAdd(S + (row & 127) * SLD + vl, -(gs * rs) * mass);
         }
       }
       __syncthreads();
@@ -798,7 +815,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
     for (int vt = g; vt < a.nvt; vt += 8)
       lse_merge(m, s, a.pm[int64_t(vt) * a.c_pad + r], a.ps[int64_t(vt) * a.c_pad + r]);
     for (int k = g; k < a.K; k += 8)
-      gz += a.p[int64_t(r) * a.K + k] * a.zsel[int64_t(r) * a.K + k];
+      gz += a.p[int64_t(r) * a.K + k] * a.zsel[int64_t(r) * a.KE + k];
   }
   sm[g][rl] = m;
   ss[g][rl] = s;
@@ -811,7 +828,15 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
     }
     const float lse = m + logf(s);
     a.lse[r] = lse;
-    a.rowkl[r] = a.h[r] - gz + lse;
+    float l = a.h[r] - gz + lse;  // KL_n
+    if (a.labels != nullptr) {    // the loss terms: scale (alpha KL_n + beta CE_n)
+      const int y = a.labels[r];
+      const float ce = unsigned(y) < unsigned(a.V) ? lse - a.zsel[int64_t(r) * a.KE + a.K] : 0.f;
+      l = a.scale * (a.alpha * l + a.beta * ce);
+    } else if (a.alpha != 1.f || a.scale != 1.f) {
+      l = a.scale * (a.alpha * l);
+    }
+    a.rowkl[r] = l;
   }
 }
 
@@ -834,19 +859,33 @@ __global__ __launch_bounds__(NT) void dense_combine_kernel(DenseCombineArgs a) {
   a.rowkl[r] = t1 / t0 - lse_t + lse;
 }
 
-__global__ __launch_bounds__(NT) void finalize_kernel(const float* __restrict__ rowkl, int64_t N,
-                                                      float* __restrict__ loss) {
-  __shared__ double red[NT];
+// loss = sum_n w_n l_n / sum_n w_n (w_n = 1 without weights; 0 for an empty
+// or all-zero weight), summed in fp64 in a fixed order.  Also leaves
+// 1 / sum_n w_n in *inv_wsum when asked (the backward's per-row factor).
+__global__ __launch_bounds__(NT) void finalize_kernel(const float* __restrict__ rowl, const float* __restrict__ w,
+                                                      int64_t N, float* __restrict__ loss, float* inv_wsum) {
+  __shared__ double red[NT], redw[NT];
   const int tid = threadIdx.x;
-  double acc = 0.0;
-  for (int64_t i = tid; i < N; i += NT) acc += double(rowkl[i]);
+  double acc = 0.0, aw = 0.0;
+  for (int64_t i = tid; i < N; i += NT) {
+    const double wi = w != nullptr ? double(w[i]) : 1.0;
+    if (rowl != nullptr && wi != 0.0) acc += wi * double(rowl[i]);
+    aw += wi;
+  }
   red[tid] = acc;
+  redw[tid] = aw;
   __syncthreads();
   for (int o = NT / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
+    if (tid < o) {
+      red[tid] += red[tid + o];
+      redw[tid] += redw[tid + o];
+    }
     __syncthreads();
   }
-  if (tid == 0) loss[0] = N > 0 ? float(red[0] / double(N)) : 0.f;
+  if (tid == 0) {
+    if (loss != nullptr) loss[0] = redw[0] != 0.0 ? float(red[0] / redw[0]) : 0.f;
+    if (inv_wsum != nullptr) inv_wsum[0] = redw[0] != 0.0 ? float(1.0 / redw[0]) : 0.f;
+  }
 }
 
 // --------------------------------------------------------------- dH and dW ---
@@ -1083,8 +1122,9 @@ hipError_t launch_dense_combine(const DenseCombineArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const float* rowkl, int64_t N, float* loss, hipStream_t s) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(NT), 0, s, rowkl, N, loss);
+hipError_t launch_finalize(const float* rowl, const float* w, int64_t N, float* loss, float* inv_wsum,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(NT), 0, s, rowl, w, N, loss, inv_wsum);
   return hipGetLastError();
 }
 

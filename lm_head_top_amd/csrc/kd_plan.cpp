@@ -82,12 +82,13 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
   p.off_p = take(size_t(p.c_pad) * K * 4);
   p.off_h = take(size_t(p.c_pad) * 4);
   p.off_boff = take(size_t(p.npt) * size_t(p.nvt + 1) * 4);
-  p.off_ent = take(size_t(p.npt) * kTile * K * 4);
+  p.off_scalar = take(256);  // 1 / sum of the row weights
+  p.off_ent = take(size_t(p.npt) * kTile * (K + 1) * 4);  // K cached ids and a label per row
   const size_t shared_end = off;
   // forward-only region
   p.off_pm = take(size_t(p.nvt) * p.c_pad * 4);
   p.off_ps = take(size_t(p.nvt) * p.c_pad * 4);
-  p.off_zsel = take(size_t(p.c_pad) * K * 4);
+  p.off_zsel = take(size_t(p.c_pad) * (K + 1) * 4);
   p.off_rowkl = take(size_t(N > 0 ? N : 1) * 4);
   const size_t fwd_end = off;
   // backward-only region aliases the forward-only one

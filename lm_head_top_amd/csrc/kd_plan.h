@@ -27,7 +27,7 @@ struct Plan {
   int dh_split = 1;    // split-K factor of the dH GEMM
   int dw_group = 1;    // consecutive chunks whose G rows feed one dW GEMM (K = dw_group * chunk)
   // workspace byte offsets
-  size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0;  // shared by fwd and bwd
+  size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0, off_scalar = 0;  // shared by fwd and bwd
   size_t off_pm = 0, off_ps = 0, off_zsel = 0, off_rowkl = 0;  // forward only
   size_t off_g = 0, off_dhp = 0;  // backward only (aliases forward)
   size_t bytes = 0;

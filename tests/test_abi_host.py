@@ -247,3 +247,39 @@ def test_dense_entry_points_reject(lib):
     b = lib.kd_dense_kl_backward
     assert b(ok, ok, ok, 0, ok, ok, None, 16, 8, 64, 1.0, 8, ok, vp(8), ok, 1 << 30,
              None) == KD_ERR_INVALID_ARG                                    # dW misaligned
+
+
+def test_ext_entry_points_reject(lib):
+    vp = ctypes.c_void_p
+    ok = vp(256)
+    f = lib.kd_topk_kl_forward_ex
+    # H, W, idx, t, N, D, V, K, T, chunk, row_weight, labels, kd_w, ce_w, flags, loss, lse, row_loss, ws, bytes, s
+    args = [ok, ok, ok, ok, 16, 8, 64, 4, 1.0, 8, None, None, 1.0, 0.0, 0, ok, ok, None, ok, 1 << 30, None]
+
+    def fwd(kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[k] = v
+        return f(*a)
+    assert fwd({14: 2}) == KD_ERR_INVALID_ARG                 # unknown flag bit
+    assert fwd({12: float("nan")}) == KD_ERR_INVALID_ARG      # kd_weight not finite
+    assert fwd({13: float("inf")}) == KD_ERR_INVALID_ARG      # ce_weight not finite
+    assert fwd({10: vp(258)}) == KD_ERR_INVALID_ARG           # row_weight misaligned
+    assert fwd({11: vp(258)}) == KD_ERR_INVALID_ARG           # labels misaligned
+    assert fwd({18: ok, 19: 16}) == KD_ERR_WORKSPACE
+    b = lib.kd_topk_kl_backward_ex
+    # H, W, idx, t, lse, g, N, D, V, K, T, chunk, row_weight, labels, kd_w, ce_w, flags, dH, dW, ws, bytes, s
+    bargs = [ok, ok, ok, ok, ok, None, 16, 8, 64, 4, 1.0, 8, None, None, 1.0, 0.0, 0, ok, ok, ok, 1 << 30,
+             None]
+
+    def bwd(kw):
+        a = list(bargs)
+        for k, v in kw.items():
+            a[k] = v
+        return b(*a)
+    assert bwd({16: 4}) == KD_ERR_INVALID_ARG
+    assert bwd({18: vp(8)}) == KD_ERR_INVALID_ARG             # dW misaligned
+    assert bwd({13: vp(2)}) == KD_ERR_INVALID_ARG             # labels misaligned
+    assert bwd({20: 16}) == KD_ERR_WORKSPACE
+    assert bwd({6: 0, 0: None, 1: None, 2: None, 3: None, 4: None, 17: None, 19: None,
+                  20: 0}) == KD_OK                               # N = 0: nothing enqueued
