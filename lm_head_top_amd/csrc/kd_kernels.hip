@@ -460,15 +460,47 @@ __global__ __launch_bounds__(NT) void teacher_kernel(TeacherArgs a) {
 // K).  Entry word: row-in-tile << 17 | id % 256 << 9 | k.  Ids outside
 // [0, V) (and negative labels) are dropped.
 constexpr int BT = 1024;  // threads of the bucketing kernel
+constexpr int BU = 8;     // entries per thread per round (loads in flight)
+constexpr int kPeel = 3;  // shared tiles merged per wave before single adds
+
 __device__ __forceinline__ int entry_id(const BucketArgs& a, const int32_t* idx, int r0, int e) {
   const int rr = e / a.KE, k = e - rr * a.KE;
   return k < a.K ? idx[int64_t(rr) * a.K + k] : a.labels[r0 + rr];
 }
 
+// cnt[b] += 1 for every lane with `valid`; returns the lane's old count (its
+// slot) when POS.  Cached ids crowd into a few vocab tiles (the frequent
+// tokens share the first tiles), and LDS atomics on one address serialize, so
+// the lanes of a wave that share the tile of the first pending lane are added
+// with one atomic, up to kPeel times; the remaining lanes add one by one.
+template <bool POS>
+__device__ __forceinline__ int tile_add(int* cnt, int b, bool valid, int lane) {
+  bool done = !valid;
+  int pos = 0;
+#pragma unroll
+  for (int it = 0; it < kPeel; ++it) {
+    const uint64_t act = __ballot(!done);
+    if (act == 0) break;  // uniform
+    const int leader = __builtin_ctzll(act);
+    const int lb = __shfl(b, leader);
+    const bool mine = !done && b == lb;
+    const uint64_t m = __ballot(mine);
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&cnt[lb], __popcll(m));
+    if (POS) base = __shfl(base, leader);
+    if (mine) {
+      pos = base + __popcll(m & ((uint64_t(1) << lane) - 1));
+      done = true;
+    }
+  }
+  if (!done) pos = atomicAdd(&cnt[b], 1);
+  return pos;
+}
+
 __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   __shared__ int cnt[kMaxVocabTiles];
-  __shared__ int part[BT];
-  const int pt = blockIdx.x, tid = threadIdx.x;
+  __shared__ int wsum[BT / 64];
+  const int pt = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = pt * kTile;
   const int nr = min(kTile, a.rows - r0);
   const int nvt = a.nvt;
@@ -476,32 +508,46 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   const int32_t* idx = a.idx + int64_t(r0) * a.K;
   for (int v = tid; v < nvt; v += BT) cnt[v] = 0;
   __syncthreads();
-  for (int e0 = 0; e0 < ne; e0 += 4 * BT) {
-    int id[4];
+  for (int e0 = 0; e0 < ne; e0 += BU * BT) {
+    int id[BU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < BU; ++u) {
       const int e = e0 + u * BT + tid;
       id[u] = e < ne ? entry_id(a, idx, r0, e) : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (unsigned(id[u]) < unsigned(a.V)) atomicAdd(&cnt[id[u] >> 8], 1);
+    for (int u = 0; u < BU; ++u) {
+      const bool ok = unsigned(id[u]) < unsigned(a.V);
+      tile_add<false>(cnt, ok ? id[u] >> 8 : 0, ok, lane);
+    }
   }
   __syncthreads();
+  // exclusive scan of the counts: each thread owns seg consecutive tiles;
+  // shuffles scan within a wave, then the 16 wave totals
   const int seg = (nvt + BT - 1) / BT;
   const int b0 = tid * seg;
   int loc = 0;
   for (int q = 0; q < seg; ++q)
     if (b0 + q < nvt) loc += cnt[b0 + q];
-  part[tid] = loc;
-  __syncthreads();
-  for (int off = 1; off < BT; off <<= 1) {
-    const int x = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += x;
-    __syncthreads();
+  int x = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  int run = part[tid] - loc;
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < BT / 64 ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < BT / 64; o <<= 1) {
+      const int y = __shfl_up(w, o);
+      if (lane >= o) w += y;
+    }
+    if (lane < BT / 64) wsum[lane] = w;
+  }
+  __syncthreads();
+  int run = (wave > 0 ? wsum[wave - 1] : 0) + x - loc;
   int32_t* bo = a.boff + int64_t(pt) * (nvt + 1);
   for (int q = 0; q < seg; ++q) {
     const int v = b0 + q;
@@ -512,24 +558,26 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
       run += c;
     }
   }
-  if (tid == BT - 1) bo[nvt] = part[BT - 1];
+  if (tid == BT - 1) bo[nvt] = wsum[BT / 64 - 1];
   __syncthreads();
   uint32_t* ent = a.ent + int64_t(pt) * kTile * a.KE;
-  for (int e0 = 0; e0 < ne; e0 += 4 * BT) {
-    int id[4];
+  for (int e0 = 0; e0 < ne; e0 += BU * BT) {
+    int id[BU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < BU; ++u) {
       const int e = e0 + u * BT + tid;
       id[u] = e < ne ? entry_id(a, idx, r0, e) : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (unsigned(id[u]) < unsigned(a.V)) {
+    for (int u = 0; u < BU; ++u) {
+      const bool ok = unsigned(id[u]) < unsigned(a.V);
+      const int pos = tile_add<true>(cnt, ok ? id[u] >> 8 : 0, ok, lane);
+      if (ok) {
         const int e = e0 + u * BT + tid;
         const int rr = e / a.KE, k = e - rr * a.KE;
-        const int pos = atomicAdd(&cnt[id[u] >> 8], 1);
         ent[pos] = (uint32_t(rr) << 17) | (uint32_t(id[u] & (kTile - 1)) << 9) | uint32_t(k);
       }
+    }
   }
 }
 
@@ -806,22 +854,43 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
 
 // ----------------------------------------------------------------- combine ---
 
+// One block per CR positions; its CG thread groups each merge every CG-th
+// vocabulary tile's (max, sum exp) partial and every CG-th cached entry, then
+// two LDS rounds merge the groups (8 groups each, then the 8 results), so each
+// thread's chain of dependent merges is short.  Blocks are dealt so that the
+// blocks reading one 128-byte line of partials share an XCD's L2.
+constexpr int CR = 4;        // positions per combine block
+constexpr int CG = NT / CR;  // thread groups per position
+static_assert(CG == 64, "two merge rounds of 8");
+
 __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
-  __shared__ float sm[8][32], ss[8][32], sg[8][32];
-  const int tid = threadIdx.x, rl = tid & 31, g = tid >> 5;
-  const int r = blockIdx.x * 32 + rl;
+  __shared__ float sm[CG][CR], ss[CG][CR], sg[CG][CR];
+  const int tid = threadIdx.x, rl = tid % CR, g = tid / CR;
+  const int r = xcd_remap(blockIdx.x, gridDim.x) * CR + rl;
   float m = -INFINITY, s = 0.f, gz = 0.f;
   if (r < a.rows) {
-    for (int vt = g; vt < a.nvt; vt += 8)
+    for (int vt = g; vt < a.nvt; vt += CG)
       lse_merge(m, s, a.pm[int64_t(vt) * a.c_pad + r], a.ps[int64_t(vt) * a.c_pad + r]);
-    for (int k = g; k < a.K; k += 8)
+    for (int k = g; k < a.K; k += CG)
       gz += a.p[int64_t(r) * a.K + k] * a.zsel[int64_t(r) * a.KE + k];
   }
   sm[g][rl] = m;
   ss[g][rl] = s;
   sg[g][rl] = gz;
   __syncthreads();
+  if (g < 8) {
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+      lse_merge(m, s, sm[g + 8 * q][rl], ss[g + 8 * q][rl]);
+      gz += sg[g + 8 * q][rl];
+    }
+    sm[g][rl] = m;
+    ss[g][rl] = s;
+    sg[g][rl] = gz;
+  }
+  __syncthreads();
   if (g == 0 && r < a.rows) {
+#pragma unroll
     for (int q = 1; q < 8; ++q) {
       lse_merge(m, s, sm[q][rl], ss[q][rl]);
       gz += sg[q][rl];
@@ -1113,7 +1182,7 @@ hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(ceil_div(a.rows, 32))), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(ceil_div(a.rows, CR))), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
