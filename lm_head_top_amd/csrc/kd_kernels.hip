@@ -459,70 +459,53 @@ __global__ __launch_bounds__(NT) void teacher_kernel(TeacherArgs a) {
 // has KE entries: its K cached ids (k < K) and, with labels, the label (k =
 // K).  Entry word: row-in-tile << 17 | id % 256 << 9 | k.  Ids outside
 // [0, V) (and negative labels) are dropped.
-constexpr int BT = 1024;  // threads of the bucketing kernel
-constexpr int BU = 8;     // entries per thread per round (loads in flight)
-constexpr int kPeel = 3;  // shared tiles merged per wave before single adds
-
-__device__ __forceinline__ int entry_id(const BucketArgs& a, const int32_t* idx, int r0, int e) {
-  const int rr = e / a.KE, k = e - rr * a.KE;
-  return k < a.K ? idx[int64_t(rr) * a.K + k] : a.labels[r0 + rr];
-}
-
-// cnt[b] += 1 for every lane with `valid`; returns the lane's old count (its
-// slot) when POS.  Cached ids crowd into a few vocab tiles (the frequent
-// tokens share the first tiles), and LDS atomics on one address serialize, so
-// the lanes of a wave that share the tile of the first pending lane are added
-// with one atomic, up to kPeel times; the remaining lanes add one by one.
-template <bool POS>
-__device__ __forceinline__ int tile_add(int* cnt, int b, bool valid, int lane) {
-  bool done = !valid;
-  int pos = 0;
-#pragma unroll
-  for (int it = 0; it < kPeel; ++it) {
-    const uint64_t act = __ballot(!done);
-    if (act == 0) break;  // uniform
-    const int leader = __builtin_ctzll(act);
-    const int lb = __shfl(b, leader);
-    const bool mine = !done && b == lb;
-    const uint64_t m = __ballot(mine);
-    int base = 0;
-    if (lane == leader) base = atomicAdd(&cnt[lb], __popcll(m));
-    if (POS) base = __shfl(base, leader);
-    if (mine) {
-      pos = base + __popcll(m & ((uint64_t(1) << lane) - 1));
-      done = true;
-    }
-  }
-  if (!done) pos = atomicAdd(&cnt[b], 1);
-  return pos;
-}
+//
+// The cached ids are walked in their stored order (entry e of the tile is
+// idx[r0 * K + e]); each thread loads all its entries at once (up to K = 128;
+// more take further rounds) and keeps them in registers for the scatter.  The
+// sorted list is built in LDS and copied out with coalesced stores when it
+// fits (KE <= 120), else scattered straight to memory.
+constexpr int BT = 1024;              // threads of the bucketing kernel
+constexpr int BU = 32;                // entries per thread per round
+constexpr int kBucketStage = 120 * kTile;  // entries of the LDS copy (120 KiB)
 
 __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   __shared__ int cnt[kMaxVocabTiles];
   __shared__ int wsum[BT / 64];
+  __shared__ uint32_t stage[kBucketStage];
   const int pt = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = pt * kTile;
   const int nr = min(kTile, a.rows - r0);
   const int nvt = a.nvt;
-  const int ne = nr * a.KE;
+  const int nk = nr * a.K;  // cached entries of the tile
   const int32_t* idx = a.idx + int64_t(r0) * a.K;
-  for (int v = tid; v < nvt; v += BT) cnt[v] = 0;
-  __syncthreads();
-  for (int e0 = 0; e0 < ne; e0 += BU * BT) {
-    int id[BU];
+  const float invK = 1.f / float(a.K);
+  int id[BU];
+  auto load = [&](int e0) {
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
       const int e = e0 + u * BT + tid;
-      id[u] = e < ne ? entry_id(a, idx, r0, e) : -1;
+      id[u] = e < nk ? idx[e] : -1;
     }
-#pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const bool ok = unsigned(id[u]) < unsigned(a.V);
-      tile_add<false>(cnt, ok ? id[u] >> 8 : 0, ok, lane);
-    }
-  }
+  };
+  load(0);  // in flight while the counters are cleared
+  for (int v = tid; v < nvt; v += BT) cnt[v] = 0;
   __syncthreads();
-  // exclusive scan of the counts: each thread owns seg consecutive tiles;
+  for (int e0 = 0;;) {
+#pragma unroll
+    for (int u = 0; u < BU; ++u)
+      if (unsigned(id[u]) < unsigned(a.V)) atomicAdd(&cnt[id[u] >> 8], 1);
+    e0 += BU * BT;
+    if (e0 >= nk) break;
+    load(e0);
+  }
+  if (a.labels != nullptr)
+    for (int rr = tid; rr < nr; rr += BT) {
+      const int y = a.labels[r0 + rr];
+      if (unsigned(y) < unsigned(a.V)) atomicAdd(&cnt[y >> 8], 1);
+    }
+  __syncthreads();
+  // exclusive scan of the counters: each thread owns seg consecutive ones;
   // shuffles scan within a wave, then the 16 wave totals
   const int seg = (nvt + BT - 1) / BT;
   const int b0 = tid * seg;
@@ -548,6 +531,7 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   }
   __syncthreads();
   int run = (wave > 0 ? wsum[wave - 1] : 0) + x - loc;
+  const int total = wsum[BT / 64 - 1];
   int32_t* bo = a.boff + int64_t(pt) * (nvt + 1);
   for (int q = 0; q < seg; ++q) {
     const int v = b0 + q;
@@ -558,26 +542,38 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
       run += c;
     }
   }
-  if (tid == BT - 1) bo[nvt] = wsum[BT / 64 - 1];
+  if (tid == BT - 1) bo[nvt] = total;
   __syncthreads();
   uint32_t* ent = a.ent + int64_t(pt) * kTile * a.KE;
-  for (int e0 = 0; e0 < ne; e0 += BU * BT) {
-    int id[BU];
+  const bool in_lds = nr * a.KE <= kBucketStage;  // uniform
+  uint32_t* dst = in_lds ? stage : ent;
+  const bool multi = nk > BU * BT;  // else the ids are still in registers
+  for (int e0 = 0; e0 < nk; e0 += BU * BT) {
+    if (multi) load(e0);
 #pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const int e = e0 + u * BT + tid;
-      id[u] = e < ne ? entry_id(a, idx, r0, e) : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const bool ok = unsigned(id[u]) < unsigned(a.V);
-      const int pos = tile_add<true>(cnt, ok ? id[u] >> 8 : 0, ok, lane);
-      if (ok) {
+    for (int u = 0; u < BU; ++u)
+      if (unsigned(id[u]) < unsigned(a.V)) {
         const int e = e0 + u * BT + tid;
-        const int rr = e / a.KE, k = e - rr * a.KE;
-        ent[pos] = (uint32_t(rr) << 17) | (uint32_t(id[u] & (kTile - 1)) << 9) | uint32_t(k);
+        // e / K through the float reciprocal: (e + 0.5) / K < 256 misses every
+        // integer by at least 1/(2K) >= 2^-9, and the two roundings err by less
+        // than 2^-15 (checked exhaustively for every K and e on the host)
+        const int rr = int((float(e) + 0.5f) * invK);
+        const int k = e - rr * a.K;
+        const int pos = atomicAdd(&cnt[id[u] >> 8], 1);
+        dst[pos] = (uint32_t(rr) << 17) | (uint32_t(id[u] & (kTile - 1)) << 9) | uint32_t(k);
+      }
+  }
+  if (a.labels != nullptr)
+    for (int rr = tid; rr < nr; rr += BT) {
+      const int y = a.labels[r0 + rr];
+      if (unsigned(y) < unsigned(a.V)) {
+        const int pos = atomicAdd(&cnt[y >> 8], 1);
+        dst[pos] = (uint32_t(rr) << 17) | (uint32_t(y & (kTile - 1)) << 9) | uint32_t(a.K);
       }
     }
+  if (in_lds) {
+    __syncthreads();
+    for (int i = tid; i < total; i += BT) ent[i] = stage[i];
   }
 }
 
