@@ -464,19 +464,29 @@ __global__ __launch_bounds__(NT) void teacher_kernel(TeacherArgs a) {
 // idx[r0 * K + e]); each thread loads all its entries at once (up to K = 128;
 // more take further rounds) and keeps them in registers for the scatter.  The
 // sorted list is built in LDS and copied out with coalesced stores when it
-// fits (KE <= 120), else scattered straight to memory.
-constexpr int BT = 1024;              // threads of the bucketing kernel
-constexpr int BU = 32;                // entries per thread per round
-constexpr int kBucketStage = 120 * kTile;  // entries of the LDS copy (120 KiB)
+// fits (KE <= 118), else scattered straight to memory.  Cached ids crowd into
+// the first vocab tiles (frequent tokens) and LDS atomics on one address
+// serialize, so each tile gets bs counters (lane % bs picks one; bs = 16 down
+// to 1 as the vocabulary grows, within the LDS left); the scan runs over
+// (tile, counter) in order, so a tile's entries stay contiguous.
+constexpr int BT = 1024;                   // threads of the bucketing kernel
+constexpr int BU = 32;                     // entries per thread per round
+constexpr int kBucketStage = 118 * kTile;  // entries of the LDS copy
+constexpr int kBucketCnt = 10240;          // counters (>= kMaxVocabTiles)
+static_assert(kBucketCnt >= kMaxVocabTiles, "one counter per vocab tile at least");
 
 __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
-  __shared__ int cnt[kMaxVocabTiles];
+  __shared__ int cnt[kBucketCnt];
   __shared__ int wsum[BT / 64];
   __shared__ uint32_t stage[kBucketStage];
   const int pt = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = pt * kTile;
   const int nr = min(kTile, a.rows - r0);
   const int nvt = a.nvt;
+  int bsh = 4;  // log2 of the counters per tile
+  while (bsh > 0 && (nvt << bsh) > kBucketCnt) --bsh;
+  const int nc = nvt << bsh;
+  const int sub = lane & ((1 << bsh) - 1);
   const int nk = nr * a.K;  // cached entries of the tile
   const int32_t* idx = a.idx + int64_t(r0) * a.K;
   const float invK = 1.f / float(a.K);
@@ -489,12 +499,12 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
     }
   };
   load(0);  // in flight while the counters are cleared
-  for (int v = tid; v < nvt; v += BT) cnt[v] = 0;
+  for (int v = tid; v < nc; v += BT) cnt[v] = 0;
   __syncthreads();
   for (int e0 = 0;;) {
 #pragma unroll
     for (int u = 0; u < BU; ++u)
-      if (unsigned(id[u]) < unsigned(a.V)) atomicAdd(&cnt[id[u] >> 8], 1);
+      if (unsigned(id[u]) < unsigned(a.V)) atomicAdd(&cnt[((id[u] >> 8) << bsh) | sub], 1);
     e0 += BU * BT;
     if (e0 >= nk) break;
     load(e0);
@@ -502,16 +512,16 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   if (a.labels != nullptr)
     for (int rr = tid; rr < nr; rr += BT) {
       const int y = a.labels[r0 + rr];
-      if (unsigned(y) < unsigned(a.V)) atomicAdd(&cnt[y >> 8], 1);
+      if (unsigned(y) < unsigned(a.V)) atomicAdd(&cnt[((y >> 8) << bsh) | sub], 1);
     }
   __syncthreads();
   // exclusive scan of the counters: each thread owns seg consecutive ones;
   // shuffles scan within a wave, then the 16 wave totals
-  const int seg = (nvt + BT - 1) / BT;
+  const int seg = (nc + BT - 1) / BT;
   const int b0 = tid * seg;
   int loc = 0;
   for (int q = 0; q < seg; ++q)
-    if (b0 + q < nvt) loc += cnt[b0 + q];
+    if (b0 + q < nc) loc += cnt[b0 + q];
   int x = loc;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -535,9 +545,9 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   int32_t* bo = a.boff + int64_t(pt) * (nvt + 1);
   for (int q = 0; q < seg; ++q) {
     const int v = b0 + q;
-    if (v < nvt) {
+    if (v < nc) {
       const int c = cnt[v];
-      bo[v] = run;
+      if ((v & ((1 << bsh) - 1)) == 0) bo[v >> bsh] = run;
       cnt[v] = run;
       run += c;
     }
@@ -559,7 +569,7 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
         // than 2^-15 (checked exhaustively for every K and e on the host)
         const int rr = int((float(e) + 0.5f) * invK);
         const int k = e - rr * a.K;
-        const int pos = atomicAdd(&cnt[id[u] >> 8], 1);
+        const int pos = atomicAdd(&cnt[((id[u] >> 8) << bsh) | sub], 1);
         dst[pos] = (uint32_t(rr) << 17) | (uint32_t(id[u] & (kTile - 1)) << 9) | uint32_t(k);
       }
   }
@@ -567,7 +577,7 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
     for (int rr = tid; rr < nr; rr += BT) {
       const int y = a.labels[r0 + rr];
       if (unsigned(y) < unsigned(a.V)) {
-        const int pos = atomicAdd(&cnt[y >> 8], 1);
+        const int pos = atomicAdd(&cnt[((y >> 8) << bsh) | sub], 1);
         dst[pos] = (uint32_t(rr) << 17) | (uint32_t(y & (kTile - 1)) << 9) | uint32_t(a.K);
       }
     }
