@@ -424,6 +424,80 @@ def keep_compare(args):
     print(json.dumps(line), flush=True)
 
 
+def blas_compare(args):
+    """The library's four GEMM kernels beside hipBLASLt (torch.mm) on the same
+    shapes of --config: the forward / backward logits GEMM (H_c W^T), the dH
+    GEMM (G_c W) and the dW GEMM of one chunk group (G^T H).  The library's
+    kernels carry their fused epilogues (online log-sum-exp, gradient, fp32
+    accumulation into dW); torch.mm writes bf16 and does nothing else.  A
+    measurement aid: per-launch averages over --steps fused steps, and the
+    median of 10 torch.mm calls."""
+    import torch
+    import lm_head_top_amd as kd
+    from synth import get_config
+    kd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    N, D, V, K, T, chunk = cfg.N, cfg.D, cfg.V, cfg.K, cfg.T, cfg.chunk
+    c = min(chunk, N)
+    rows_dw = min(N, c * -(-4096 // c))
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    W = (torch.randn((V, D), generator=g, device=dev) * D ** -0.5).to(torch.bfloat16)
+    H, idx, t = _gpu_inputs(torch, N, D, V, K, args.seed + 1, dev)
+    dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kd.workspace_size(N, D, V, K, chunk), dtype=torch.uint8, device=dev)
+
+    def step():
+        loss, lse = kd.forward(H, W, idx, t, T, chunk, workspace=ws)
+        kd.backward(H, W, idx, t, lse, None, T, chunk, dW=dW, workspace=ws)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    kd.profile_enable(GEMM_KERNELS)
+    for k in GEMM_KERNELS:
+        kd.profile_read(k)
+    for _ in range(max(args.steps, 1)):
+        step()
+    torch.cuda.synchronize()
+    kd.profile_enable(None)
+    ours = {k: kd.profile_read(k) for k in GEMM_KERNELS}
+    Hc = H[:c]
+    Gc = torch.randn((c, V), generator=g, device=dev).to(torch.bfloat16)
+    G = torch.randn((rows_dw, V), generator=g, device=dev).to(torch.bfloat16)
+    Hg = H[:rows_dw]
+    shapes = {"logits_fwd": (lambda: torch.mm(Hc, W.t()), 2 * c * D * V),
+              "logits_bwd": (lambda: torch.mm(Hc, W.t()), 2 * c * D * V),
+              "dh": (lambda: torch.mm(Gc, W), 2 * c * D * V),
+              "dw": (lambda: torch.mm(G.t(), Hg), 2 * rows_dw * D * V)}
+    out = {}
+    for k, (fn, flops) in shapes.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        blas_ms = times[5]
+        ms, n = ours[k]
+        ours_ms = ms / n
+        out[k] = {"ours_ms": round(ours_ms, 4), "ours_tflops": round(flops / ours_ms / 1e9, 1),
+                  "hipblaslt_ms": round(blas_ms, 4), "hipblaslt_tflops": round(flops / blas_ms / 1e9, 1),
+                  "gflop": round(flops / 1e9, 1)}
+        log(f"{k}: {out[k]}")
+    line = {"mode": "gemm_vs_hipblaslt", "config": {**_config_doc(cfg, args.seed), "dw_rows": rows_dw},
+            "kernels": out}
+    print(json.dumps(line), flush=True)
+
+
 def loss_ext(args):
     """The loss extensions on --config beside the plain loss, same inputs: a
     0/1 position mask (about 10% of positions masked, as padding would), a
@@ -575,6 +649,8 @@ def main():
     ap.add_argument("--loss-ext", action="store_true",
                     help="the loss extensions (mask, hard-label mix, T^2) beside the plain loss "
                          "on --config")
+    ap.add_argument("--blas-compare", action="store_true",
+                    help="the four GEMM kernels beside hipBLASLt (torch.mm) on the same shapes of --config")
     args = ap.parse_args()
     if args.gpus != 1 and not (args.stats_from or args.traffic_from):
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the loss runs on one "
@@ -583,6 +659,9 @@ def main():
         sys.exit(2)
     if args.loss_ext:
         loss_ext(args)
+        return
+    if args.blas_compare:
+        blas_compare(args)
         return
     if args.keep_compare or args.dense_teacher:
         (keep_compare if args.keep_compare else dense_teacher)(args)
