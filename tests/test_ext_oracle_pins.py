@@ -108,9 +108,26 @@ def pin_gradient_rows_sum_to_zero():
     assert np.allclose(G.sum(axis=1), 0.0, atol=1e-12)
 
 
+def pin_rows_form_equals_dense():
+    """The per-row form (used at full size) gives the dense form's lse, row
+    loss and dH rows, with the weight normaliser taken over all positions."""
+    H, W, idx, t, _, _ = _case(11, N=30, V=50, K=7)
+    r = np.random.default_rng(12)
+    labels = r.integers(0, 50, 30).astype(np.int32)
+    labels[::4] = -1
+    w = r.random(30) * 2.0
+    kw = dict(labels=labels, weights=w, alpha=0.6, beta=0.8, scale_T2=True, grad_loss=0.4)
+    dense = E.forward_backward_ext(H, W, idx, t, 1.7, **kw)
+    rows = [0, 3, 17, 29]
+    part = E.rows_ext(H, W, idx, t, rows, 1.7, **kw)
+    assert np.allclose(part["lse"], dense["lse"][rows], rtol=1e-13, atol=0)
+    assert np.allclose(part["row_loss"], dense["row_loss"][rows], rtol=1e-12, atol=1e-15)
+    assert np.allclose(part["dH"], dense["dH"][rows], rtol=1e-12, atol=1e-15)
+
+
 PINS = [pin_defaults_reduce_to_base, pin_pure_ce_is_torch_cross_entropy,
         pin_mixed_weighted_loss_against_autograd, pin_t2_scaling, pin_mask_equals_subset,
-        pin_gradient_rows_sum_to_zero]
+        pin_gradient_rows_sum_to_zero, pin_rows_form_equals_dense]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)

@@ -63,6 +63,10 @@ CASES = {
                                    "some_missing", "weights"),
     "ce_only": (KDConfig("ce", N=300, D=136, V=1000, K=16, chunk=128, T=1.0, ids="uniform", cfg_id=8),
                 1.0, None, 0.0, 1.0, False, "all", None),
+    # K at its limit plus a label: 257 entries per position (several load
+    # rounds and the direct-scatter path of the bucketing kernel)
+    "max_k_with_labels": (KDConfig("maxk", N=300, D=64, V=2000, K=256, chunk=256, T=1.0, ids="uniform",
+                                   cfg_id=10), 1.5, 0.8, 0.5, 0.5, True, "some_missing", "weights"),
 }
 
 
@@ -164,3 +168,52 @@ def test_mask_at_full_size_matches_the_masked_subset():
     say(f"  loss rel {lr:.2e}; dH (kept rows) {eh:.2e}; dW {ew:.2e}; max |dH| on masked rows {dead}")
     assert lr <= LOSS_RTOL and eh <= GRAD_RTOL and ew <= GRAD_RTOL
     assert dead == 0.0
+
+
+def test_ext_full_size_large_vocab_sampled_rows():
+    """Large-vocabulary workload (N=32768, D=2880, V=201088, chunk 2048) with
+    weights (10% zero), labels (5% missing, some in the vocabulary's tail
+    tile and at V - 1), kd 0.6 / ce 0.4 and T = 2 with T^2: sampled rows
+    (lse, row loss, dH row) against the oracle's per-row form, the loss
+    against the weighted mean of the kernel's own row losses, and the columns
+    of dW summing to zero (every row of G does)."""
+    import torch
+    import lm_head_top_amd as kd
+    cfg = get_config("large_vocab")
+    T = 2.0
+    say(f"case ext full size large_vocab: N={cfg.N} D={cfg.D} V={cfg.V} K={cfg.K} chunk={cfg.chunk} T={T}")
+    inp = make_inputs(cfg, 0)
+    rng = np.random.default_rng(31)
+    y = rng.integers(0, cfg.V, cfg.N).astype(np.int32)
+    y[rng.random(cfg.N) < 0.05] = -1
+    tail = rng.choice(cfg.N, 64, replace=False)
+    y[tail] = rng.integers(200960, cfg.V, 64)
+    y[tail[:4]] = cfg.V - 1
+    w = (rng.random(cfg.N) * 2.0).astype(np.float32)
+    w[rng.random(cfg.N) < 0.1] = 0.0
+    rows = sorted(set([0, cfg.N - 1] + tail[:3].tolist() + np.nonzero(y < 0)[0][:2].tolist()
+                      + np.nonzero(w == 0)[0][:1].tolist() + rng.integers(0, cfg.N, 3).tolist()))
+    H, W, idx, t = to_device(inp)
+    yt = torch.from_numpy(y).cuda()
+    wt = torch.from_numpy(w).cuda()
+    kw = dict(row_weight=wt, labels=yt, kd_weight=0.6, ce_weight=0.4, scale_T2=True)
+    loss, lse, row_loss = kd.forward_ex(H, W, idx, t, T, cfg.chunk, want_row_loss=True, **kw)
+    dH, dW = kd.backward_ex(H, W, idx, t, lse, None, T, cfg.chunk, **kw)
+    torch.cuda.synchronize()
+    ref = E.rows_ext(inp["H"], inp["W"], inp["idx"], inp["t"], rows, T, labels=y, weights=w.astype(np.float64),
+                     alpha=0.6, beta=0.4, scale_T2=True)
+    g_lse = lse.double().cpu().numpy()[rows]
+    g_rl = row_loss.double().cpu().numpy()[rows]
+    g_dh = bf16_tensor_to_f64(dH[rows])
+    e_lse = np.max(np.abs(g_lse - ref["lse"]) / np.abs(ref["lse"]))
+    e_rl = np.max(np.abs(g_rl - ref["row_loss"]) / np.maximum(np.abs(ref["row_loss"]), 1.0))
+    e_dh = rel(g_dh, ref["dH"])
+    say(f"  rows {rows}: lse rel {e_lse:.2e}, row_loss rel {e_rl:.2e}, dH rel L2 {e_dh:.2e}")
+    assert e_lse <= LOSS_RTOL and e_rl <= LOSS_RTOL and e_dh <= GRAD_RTOL
+    rl_all = row_loss.double().cpu().numpy()
+    want = float((w.astype(np.float64) * rl_all).sum() / w.astype(np.float64).sum())
+    e_loss = abs(float(loss.item()) - want) / abs(want)
+    col = dW.double().sum(dim=0)
+    e_col = float(col.norm() / dW.double().norm())
+    say(f"  loss vs weighted mean of row losses rel {e_loss:.2e}; |sum_v dW[v,:]| / |dW| {e_col:.2e}")
+    assert e_loss <= 1e-5 and e_col <= 1e-2
