@@ -604,17 +604,38 @@ __device__ __forceinline__ void tri_merge(float& m, float& s0, float& s1, float 
   m = M;
 }
 
-// Four consecutive teacher logits t[p][v .. v+3] (fp32 or bf16), times 1/T.
-__device__ __forceinline__ float4 teacher4(const void* t, int dtype, int64_t off, float invT) {
-  float4 x;
-  if (dtype == 0) {
-    x = *reinterpret_cast<const float4*>(static_cast<const float*>(t) + off);
-  } else {
-    const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(t) + off);
-    x = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
-                    __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
-  }
-  return make_float4(x.x * invT, x.y * invT, x.z * invT, x.w * invT);
+// Four consecutive teacher logits t[p][v .. v+3] (fp32 or bf16) as loaded:
+// 16 bytes of fp32, or 8 bytes of bf16 in .x / .y.
+__device__ __forceinline__ uint4 teacher_raw(const void* t, int dtype, int64_t off) {
+  if (dtype == 0) return *reinterpret_cast<const uint4*>(static_cast<const float*>(t) + off);
+  const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(t) + off);
+  return make_uint4(h.x, h.y, 0u, 0u);
+}
+
+// The four logits of teacher_raw times 1/T.
+__device__ __forceinline__ float4 teacher_cvt(uint4 r, int dtype, float invT) {
+  if (dtype == 0)
+    return make_float4(__uint_as_float(r.x) * invT, __uint_as_float(r.y) * invT, __uint_as_float(r.z) * invT,
+                       __uint_as_float(r.w) * invT);
+  return make_float4(__uint_as_float(r.x << 16) * invT, __uint_as_float(r.x & 0xffff0000u) * invT,
+                     __uint_as_float(r.y << 16) * invT, __uint_as_float(r.y & 0xffff0000u) * invT);
+}
+
+// Loads the teacher logits of one accumulator column (position p0 + pl) for
+// all MI x 4 register groups of the wave, every load in flight at once;
+// groups past V or past the chunk read element 0 and are marked invalid.
+__device__ __forceinline__ void teacher_column(const void* t, int dtype, int64_t V, int rows, int p0, int pl,
+                                               int v0, int wm, int lane, uint4 (&raw)[MI][4],
+                                               bool (&ok)[MI][4]) {
+  const bool pok = p0 + pl < rows;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int vr = v0 + acc_row(wm, i, 4 * g, lane);
+      ok[i][g] = pok && vr < V;  // V % 4 == 0: vr < V covers vr .. vr + 3
+      raw[i][g] = teacher_raw(t, dtype, ok[i][g] ? int64_t(p0 + pl) * V + vr : 0);
+    }
 }
 
 // 0: forward epilogue, 1: backward epilogue, 2: forward epilogue that also
@@ -704,38 +725,44 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int pl = acc_col(wn, j, lane);
-        const bool prow_ok = p0 + pl < a.rows;
-        float tm = -INFINITY, t0 = 0.f, t1 = 0.f;
+        uint4 raw[MI][4];
+        bool ok[MI][4];
+        teacher_column(a.tlog, a.t_dtype, a.V, a.rows, p0, pl, v0, wm, lane, raw, ok);
+        float tm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int vr = v0 + acc_row(wm, i, 4 * g, lane);
-            if (!prow_ok || vr >= a.V) continue;
-            const float4 t4 = teacher4(a.tlog, a.t_dtype, int64_t(p0 + pl) * a.V + vr, a.invT);
-            const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
-            float m4 = fmaxf(fmaxf(tv[0], tv[1]), fmaxf(tv[2], tv[3]));
-            if (m4 > tm) {
-              const float sc = tm == -INFINITY ? 0.f : exp2_fast((tm - m4) * LOG2E);
-              t0 *= sc;
-              t1 *= sc;
-              tm = m4;
+          for (int g = 0; g < 4; ++g)
+            if (ok[i][g]) {
+              const float4 t4 = teacher_cvt(raw[i][g], a.t_dtype, a.invT);
+              tm = fmaxf(tm, fmaxf(fmaxf(t4.x, t4.y), fmaxf(t4.z, t4.w)));
             }
-            if (tm == -INFINITY) continue;
+        float t0 = 0.f, t1 = 0.f;
+        if (tm != -INFINITY) {
+          const float tmb = tm * LOG2E;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              if (tv[q] == -INFINITY) continue;
-              const float e = exp2_fast((tv[q] - tm) * LOG2E);
-              t0 += e;
-              t1 += e * (tv[q] - acc[i][j][4 * g + q]);
-            }
-          }
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              if (ok[i][g]) {
+                const float4 t4 = teacher_cvt(raw[i][g], a.t_dtype, a.invT);
+                const float tq[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  if (tq[q] != -INFINITY) {
+                    const float e = exp2_fast(fmaf(tq[q], LOG2E, -tmb));
+                    t0 += e;
+                    t1 += e * (tq[q] - acc[i][j][4 * g + q]);
+                  }
+              }
+        }
         tri_merge(tm, t0, t1, __shfl_xor(tm, 32), __shfl_xor(t0, 32), __shfl_xor(t1, 32));
         if (lane < 32) {
           red[(4 + wm) * kTile + pl] = tm;
           red[(6 + wm) * kTile + pl] = t0;
           red[(8 + wm) * kTile + pl] = t1;
         }
+        __builtin_amdgcn_sched_barrier(0);  // one column's loads in flight at a time
       }
     }
     __syncthreads();
@@ -802,20 +829,22 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int pl = acc_col(wn, j, lane);
-        if (p0 + pl >= a.rows) continue;
-        const float tl2 = a.lse_t[p0 + pl] * LOG2E;
+        uint4 raw[MI][4];
+        bool ok[MI][4];
+        teacher_column(a.tlog, a.t_dtype, a.V, a.rows, p0, pl, v0, wm, lane, raw, ok);
+        const float tl2 = p0 + pl < a.rows ? a.lse_t[p0 + pl] * LOG2E : 0.f;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int vr = v0 + acc_row(wm, i, 4 * g, lane);
-            if (vr >= a.V) continue;
-            const float4 t4 = teacher4(a.tlog, a.t_dtype, int64_t(p0 + pl) * a.V + vr, a.invT);
+            if (!ok[i][g]) continue;
+            const float4 t4 = teacher_cvt(raw[i][g], a.t_dtype, a.invT);
             acc[i][j][4 * g] -= gs * exp2_fast(fmaf(t4.x, LOG2E, -tl2));
             acc[i][j][4 * g + 1] -= gs * exp2_fast(fmaf(t4.y, LOG2E, -tl2));
             acc[i][j][4 * g + 2] -= gs * exp2_fast(fmaf(t4.z, LOG2E, -tl2));
             acc[i][j][4 * g + 3] -= gs * exp2_fast(fmaf(t4.w, LOG2E, -tl2));
           }
+        __builtin_amdgcn_sched_barrier(0);  // one column's loads in flight at a time
       }
     }
     for (int h = 0; h < 2; ++h) {
@@ -917,21 +946,50 @@ __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
 
 // Dense teacher: lse of the student and of the teacher from the vocab-tile
 // partials, and KL_n = sum_v p (a - z) - lse_a + lse_z with
-// sum_v p (a - z) = S1 / S0.
+// sum_v p (a - z) = S1 / S0.  Laid out like combine_kernel: CR positions per
+// block, CG groups each merging every CG-th vocab tile, then two LDS rounds.
 __global__ __launch_bounds__(NT) void dense_combine_kernel(DenseCombineArgs a) {
-  const int r = blockIdx.x * NT + threadIdx.x;
-  if (r >= a.rows) return;
+  __shared__ float sm[CG][CR], ss[CG][CR], stm[CG][CR], st0[CG][CR], st1[CG][CR];
+  const int tid = threadIdx.x, rl = tid % CR, g = tid / CR;
+  const int r = xcd_remap(blockIdx.x, gridDim.x) * CR + rl;
   float m = -INFINITY, s = 0.f, tm = -INFINITY, t0 = 0.f, t1 = 0.f;
-  for (int vt = 0; vt < a.nvt; ++vt) {
-    const int64_t o = int64_t(vt) * a.c_pad + r;
-    lse_merge(m, s, a.pm[o], a.ps[o]);
-    tri_merge(tm, t0, t1, a.tm[o], a.ts0[o], a.ts1[o]);
+  if (r < a.rows)
+    for (int vt = g; vt < a.nvt; vt += CG) {
+      const int64_t o = int64_t(vt) * a.c_pad + r;
+      lse_merge(m, s, a.pm[o], a.ps[o]);
+      tri_merge(tm, t0, t1, a.tm[o], a.ts0[o], a.ts1[o]);
+    }
+  sm[g][rl] = m;
+  ss[g][rl] = s;
+  stm[g][rl] = tm;
+  st0[g][rl] = t0;
+  st1[g][rl] = t1;
+  __syncthreads();
+  if (g < 8) {
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+      lse_merge(m, s, sm[g + 8 * q][rl], ss[g + 8 * q][rl]);
+      tri_merge(tm, t0, t1, stm[g + 8 * q][rl], st0[g + 8 * q][rl], st1[g + 8 * q][rl]);
+    }
+    sm[g][rl] = m;
+    ss[g][rl] = s;
+    stm[g][rl] = tm;
+    st0[g][rl] = t0;
+    st1[g][rl] = t1;
   }
-  const float lse = m + logf(s);
-  const float lse_t = tm + logf(t0);
-  a.lse[r] = lse;
-  a.lse_t[r] = lse_t;
-  a.rowkl[r] = t1 / t0 - lse_t + lse;
+  __syncthreads();
+  if (g == 0 && r < a.rows) {
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+      lse_merge(m, s, sm[q][rl], ss[q][rl]);
+      tri_merge(tm, t0, t1, stm[q][rl], st0[q][rl], st1[q][rl]);
+    }
+    const float lse = m + logf(s);
+    const float lse_t = tm + logf(t0);
+    a.lse[r] = lse;
+    a.lse_t[r] = lse_t;
+    a.rowkl[r] = t1 / t0 - lse_t + lse;
+  }
 }
 
 // loss = sum_n w_n l_n / sum_n w_n (w_n = 1 without weights; 0 for an empty
@@ -1193,7 +1251,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dense_combine(const DenseCombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(dense_combine_kernel, dim3(unsigned(ceil_div(a.rows, NT))), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(dense_combine_kernel, dim3(unsigned(ceil_div(a.rows, CR))), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
