@@ -38,7 +38,7 @@ def _sample_rows(N, n=6, seed=0):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["toy", "large_vocab", "long"])
+@pytest.mark.parametrize("name", ["toy", "large_vocab", "long", "very_long"])
 def test_full_size_sampled_rows(name):
     import torch
     import lm_head_top_amd as kd
