@@ -28,14 +28,23 @@ hipError_t timed(int id, hipStream_t s, F&& launch) {
     mask = g_prof_mask;
   }
   if (!(mask & (1u << id))) return launch();
-  EventPair ev{};
-  if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess) return hipErrorUnknown;
-  if (hipEventRecord(ev.a, s) != hipSuccess) return hipErrorUnknown;
-  const hipError_t e = launch();
-  if (hipEventRecord(ev.b, s) != hipSuccess) return hipErrorUnknown;
+  EventPair ev{nullptr, nullptr};
+  auto drop = [&ev](hipError_t err) {
+    if (ev.a != nullptr) (void)hipEventDestroy(ev.a);
+    if (ev.b != nullptr) (void)hipEventDestroy(ev.b);
+    return err;
+  };
+  hipError_t e = hipEventCreate(&ev.a);
+  if (e == hipSuccess) e = hipEventCreate(&ev.b);
+  if (e == hipSuccess) e = hipEventRecord(ev.a, s);
+  if (e != hipSuccess) return drop(e);
+  e = launch();
+  if (e != hipSuccess) return drop(e);
+  e = hipEventRecord(ev.b, s);
+  if (e != hipSuccess) return drop(e);
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_events[id].push_back(ev);
-  return e;
+  return hipSuccess;
 }
 
 // The HIP error behind the calling thread's most recent KD_ERR_HIP.
@@ -298,19 +307,9 @@ kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W, const int32_t
                              const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
                              float T, int64_t chunk, float* loss, float* lse, float* row_kl,
                              void* workspace, size_t workspace_bytes, void* hip_stream) {
-  kd::Plan p;
-  kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
-  if (st != KD_OK) return st;
-  st = check_forward_args(p, H, W, topk_idx, topk_logit, N, loss, lse, row_kl, workspace, workspace_bytes,
-                          p.bytes);
-  if (st != KD_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (N == 0) {
-    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
-    return KD_OK;
-  }
-  return run_forward(p, H, W, topk_idx, topk_logit, N, D, V, K, T, loss, lse, row_kl,
-                     static_cast<char*>(workspace), nullptr, nullptr, s);
+  // the extended loss at its neutral settings: no weights, no labels, kd_weight 1
+  return kd_topk_kl_forward_ex(H, W, topk_idx, topk_logit, N, D, V, K, T, chunk, nullptr, nullptr, 1.f, 0.f, 0,
+                               loss, lse, row_kl, workspace, workspace_bytes, hip_stream);
 }
 
 size_t kd_topk_kl_keep_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int64_t chunk) {
@@ -381,19 +380,8 @@ kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_
                               int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
                               uint16_t* dH, float* dW, void* workspace, size_t workspace_bytes,
                               void* hip_stream) {
-  kd::Plan p;
-  const kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
-  if (st != KD_OK) return st;
-  if (bad_ptr(dW, 16)) return KD_ERR_INVALID_ARG;
-  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(topk_idx, 4) ||
-                bad_ptr(topk_logit, 4) || bad_ptr(lse, 4) || bad_ptr(dH, 16)))
-    return KD_ERR_INVALID_ARG;
-  if (grad_loss != nullptr && !kd::aligned(grad_loss, 4)) return KD_ERR_INVALID_ARG;
-  if (N > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return KD_ERR_WORKSPACE;
-  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
-  if (N == 0) return KD_OK;  // nothing to accumulate
-  return run_backward(p, H, W, topk_idx, topk_logit, nullptr, 0, lse, nullptr, grad_loss, N, D, V, K, T,
-                      dH, dW, static_cast<char*>(workspace), static_cast<hipStream_t>(hip_stream));
+  return kd_topk_kl_backward_ex(H, W, topk_idx, topk_logit, lse, grad_loss, N, D, V, K, T, chunk, nullptr,
+                                nullptr, 1.f, 0.f, 0, dH, dW, workspace, workspace_bytes, hip_stream);
 }
 
 kd_status kd_topk_kl_forward_ex(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
