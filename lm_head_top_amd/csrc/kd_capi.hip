@@ -187,9 +187,9 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
   return KD_OK;
 }
 
-// The backward's chunk loop: recompute each chunk's logits, form G_c (top-K
-// cache, or a dense teacher when tlog is set), dH_c = G_c W, and every
-// dw_group chunks dW += G^T H.
+// The backward's chunk loop: recompute each chunk's logits and form G_c (top-K
+// cache, or a dense teacher when tlog is set); every dw_group chunks, dH of
+// the group = G W and dW += G^T H.
 kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
                        const float* topk_logit, const void* tlog, int t_dtype, const float* lse,
                        const float* lse_t, const float* grad_loss, int64_t N, int64_t D, int64_t V,
@@ -207,15 +207,16 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
   const float g_scale = ext.row_w != nullptr ? float(double(ext.scale) / double(T))
                                              : float(double(ext.scale) / (double(N) * double(T)));
   const int ktiles = int(p.Vp / kd::gemm_bk());
-  const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
+  const int kps = (ktiles + p.grp_split - 1) / p.grp_split;
   const size_t esz = t_dtype == KD_DTYPE_F32 ? 4 : 2;
   if (ext.row_w != nullptr)
     KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(nullptr, ext.row_w, N, nullptr, inv_wsum, s));
   const int KE = K + (ext.labels != nullptr ? 1 : 0);
 
   // The G rows of up to dw_group consecutive chunks are kept one after
-  // another (position order, row stride Vp) and feed one dW GEMM with K = the
-  // group's positions; H rows of the group are consecutive in H already.
+  // another (position order, row stride Vp) and feed one dH GEMM (the group's
+  // rows of dH) and one dW GEMM with K = the group's positions; H rows of the
+  // group are consecutive in H already.
   int gj = 0;
   int64_t group_row0 = 0;
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
@@ -268,15 +269,15 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
     la.beta = ext.beta;
     la.G = Gc;
     KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
-    kd::DhArgs da{Gc, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D, p.c_pad};
-    KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
-    if (p.dh_split > 1)
-      KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
-                kd::launch_dh_reduce(dhp, p.dh_split, rows, int(D), p.c_pad, dH + row0 * D, s));
     ++gj;
     const bool last = row0 + p.chunk >= N;
     if (gj == p.dw_group || last) {
       const int grows = int(row0 + rows - group_row0);
+      kd::DhArgs da{G, W, grows, int(D), int(V), p.Vp, p.grp_split, kps, dhp, dH + group_row0 * D, p.grp_pad};
+      KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
+      if (p.grp_split > 1)
+        KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
+                  kd::launch_dh_reduce(dhp, p.grp_split, grows, int(D), p.grp_pad, dH + group_row0 * D, s));
       kd::DwArgs wa{G, H + group_row0 * D, grows, int(D), int(V), p.Vp, dW};
       KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
       gj = 0;

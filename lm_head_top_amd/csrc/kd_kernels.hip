@@ -1030,7 +1030,11 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
   const int tiles = tiles_m * tiles_n;
   const int tile = xcd_remap(blockIdx.x, tiles * a.split);
   const int sp = tile / tiles, rem = tile - sp * tiles;
-  const int tm = rem % tiles_m, tn = rem / tiles_m;
+  // bands of up to 4 row tiles, row tile fastest: the 32 tiles an XCD runs at
+  // once cover 4 row tiles x 8 column tiles, whose operand strips its L2 shares
+  const int band = rem / (4 * tiles_n), bh = min(4, tiles_m - 4 * band);
+  const int bi = rem - band * 4 * tiles_n;
+  const int tm = 4 * band + bi % bh, tn = bi / bh;
   const int k_begin = sp * a.ktiles_per_split * BK;
   int k_end = k_begin + a.ktiles_per_split * BK;
   if (k_end > a.Vp) k_end = int(a.Vp);

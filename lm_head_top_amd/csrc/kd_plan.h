@@ -24,12 +24,14 @@ struct Plan {
   int64_t nvt = 0;     // vocab tiles
   int64_t Vp = 0;      // V rounded up to kTile (row stride of G_c)
   int64_t npt = 0;     // position tiles per chunk
-  int dh_split = 1;    // split-K factor of the dH GEMM
+  int dh_split = 1;    // split-K factor of a dH GEMM over one chunk (the kept-gradient comparator)
   int dw_group = 1;    // consecutive chunks whose G rows feed one dW GEMM (K = dw_group * chunk)
+  int64_t grp_pad = 0; // dw_group * chunk rounded up to kTile: rows of a group's dH GEMM
+  int grp_split = 1;   // split-K factor of the dH GEMM over a group
   // workspace byte offsets
   size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0, off_scalar = 0;  // shared by fwd and bwd
   size_t off_pm = 0, off_ps = 0, off_zsel = 0, off_rowkl = 0;  // forward only
-  size_t off_g = 0, off_dhp = 0;  // backward only (aliases forward)
+  size_t off_g = 0, off_dhp = 0;  // backward only (aliases forward); dhp: [grp_split, grp_pad, D]
   size_t bytes = 0;
 };
 
