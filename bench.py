@@ -27,6 +27,7 @@ METRIC = "fused top-K KL fwd+bwd tokens/s and % bf16 MFMA peak; peak HBM GiB"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 2516.6
 GEMM_KERNELS = ("logits_fwd", "logits_bwd", "dh", "dw")
+GROUP_POSITIONS = 8192  # positions per dH / dW GEMM of the library (whole chunks, at most 8)
 WORKLOAD_NAMES = {"tiny": "tiny", "toy": "toy_lm_head", "large_vocab": "large_vocab_head",
                   "long": "long_context", "very_long": "very_long_context"}
 # HBM traffic per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, with the
@@ -426,8 +427,8 @@ def keep_compare(args):
 
 def blas_compare(args):
     """The library's four GEMM kernels beside hipBLASLt (torch.mm) on the same
-    shapes of --config: the forward / backward logits GEMM (H_c W^T), the dH
-    GEMM (G_c W) and the dW GEMM of one chunk group (G^T H).  The library's
+    shapes of --config: the forward / backward logits GEMM of one chunk
+    (H_c W^T), and the dH (G W) and dW (G^T H) GEMMs of one group of chunks.  The library's
     kernels carry their fused epilogues (online log-sum-exp, gradient, fp32
     accumulation into dW); torch.mm writes bf16 and does nothing else.  A
     measurement aid: per-launch averages over --steps fused steps, and the
@@ -441,7 +442,9 @@ def blas_compare(args):
     cfg = get_config(args.config)
     N, D, V, K, T, chunk = cfg.N, cfg.D, cfg.V, cfg.K, cfg.T, cfg.chunk
     c = min(chunk, N)
-    rows_dw = min(N, c * -(-4096 // c))
+    # the library's dH and dW GEMMs run over groups of whole chunks holding at
+    # least GROUP_POSITIONS positions (at most 8 chunks), capped by N
+    rows_dw = min(N, c * min(8, -(-GROUP_POSITIONS // c)))
     g = torch.Generator(device=dev)
     g.manual_seed(args.seed)
     W = (torch.randn((V, D), generator=g, device=dev) * D ** -0.5).to(torch.bfloat16)
@@ -465,12 +468,11 @@ def blas_compare(args):
     kd.profile_enable(None)
     ours = {k: kd.profile_read(k) for k in GEMM_KERNELS}
     Hc = H[:c]
-    Gc = torch.randn((c, V), generator=g, device=dev).to(torch.bfloat16)
     G = torch.randn((rows_dw, V), generator=g, device=dev).to(torch.bfloat16)
     Hg = H[:rows_dw]
     shapes = {"logits_fwd": (lambda: torch.mm(Hc, W.t()), 2 * c * D * V),
               "logits_bwd": (lambda: torch.mm(Hc, W.t()), 2 * c * D * V),
-              "dh": (lambda: torch.mm(Gc, W), 2 * c * D * V),
+              "dh": (lambda: torch.mm(G, W), 2 * rows_dw * D * V),
               "dw": (lambda: torch.mm(G.t(), Hg), 2 * rows_dw * D * V)}
     out = {}
     for k, (fn, flops) in shapes.items():

@@ -62,17 +62,22 @@ kd_status make_dense_plan(int64_t N, int64_t D, int64_t V, float T, int64_t chun
 kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
                     Plan* plan);
 
-// Split-K factor of dH = G_c W for a chunk of `c` rows and hidden size D.
+// Split-K factor of a dH GEMM (G W) over `c` rows and hidden size D.
 int dh_split_for(int64_t c, int64_t D);
 
-// Chunks per dW GEMM: enough that K = group * chunk reaches kDwMinK, so the
-// fp32 dW read-modify-write (8 bytes per output element) is amortised over
-// at least 2 * kDwMinK flops per element; capped at kMaxDwGroup.
+// Chunks per group (one dH and one dW GEMM): enough that K = group * chunk
+// reaches kDwMinK, so the fp32 dW read-modify-write (8 bytes per output
+// element) is amortised over at least 2 * kDwMinK flops per element; capped
+// at kMaxDwGroup.  8192 positions measured 2% faster per step than 4096 at
+// the toy and long-context workloads, for 1 GiB more workspace at V = 131072.
 #ifndef KD_DW_MIN_K
-#define KD_DW_MIN_K 4096
+#define KD_DW_MIN_K 8192
 #endif
 constexpr int64_t kDwMinK = KD_DW_MIN_K;
-constexpr int kMaxDwGroup = 4;
+#ifndef KD_MAX_DW_GROUP
+#define KD_MAX_DW_GROUP 8
+#endif
+constexpr int kMaxDwGroup = KD_MAX_DW_GROUP;
 int dw_group_for(int64_t c, int64_t N);
 
 // Pointer checks shared by the entry points.

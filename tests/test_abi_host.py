@@ -62,10 +62,10 @@ def test_workspace_size_scales_with_chunk_not_N(lib):
     c = f(8192, 4096, 131072, 100, 2048)
     assert c > a
     # never O(N V): the dense fp32 grid at 32K x 131072 would be 16 GiB; the
-    # workspace is one chunk's G_c, the G^T of a group of g chunks feeding one
-    # dW GEMM (g = 4 at chunk 1024) and a W^T copy: O(chunk V + V D)
-    D, V, c, g = 4096, 131072, 1024, 4
-    assert b <= (1 + g) * c * V * 2 + V * D * 2 + (256 << 20)
+    # workspace holds the G rows of one group of g chunks feeding the dH and
+    # dW GEMMs (g = 8 at chunk 1024) plus per-chunk buffers: O(g chunk V)
+    V, c, g = 131072, 1024, 8
+    assert b <= g * c * V * 2 + (256 << 20)
 
 
 def test_workspace_size_rejects(lib):
