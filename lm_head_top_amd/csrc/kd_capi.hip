@@ -273,11 +273,16 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
     const bool last = row0 + p.chunk >= N;
     if (gj == p.dw_group || last) {
       const int grows = int(row0 + rows - group_row0);
-      kd::DhArgs da{G, W, grows, int(D), int(V), p.Vp, p.grp_split, kps, dhp, dH + group_row0 * D, p.grp_pad};
-      KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
-      if (p.grp_split > 1)
-        KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
-                  kd::launch_dh_reduce(dhp, p.grp_split, grows, int(D), p.grp_pad, dH + group_row0 * D, s));
+      // dH of the group in blocks of at most grp_pad rows
+      for (int64_t b0 = 0; b0 < grows; b0 += p.grp_pad) {
+        const int brows = int(grows - b0 < p.grp_pad ? grows - b0 : p.grp_pad);
+        uint16_t* dHb = dH + (group_row0 + b0) * D;
+        kd::DhArgs da{G + b0 * p.Vp, W, brows, int(D), int(V), p.Vp, p.grp_split, kps, dhp, dHb, p.grp_pad};
+        KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
+        if (p.grp_split > 1)
+          KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
+                    kd::launch_dh_reduce(dhp, p.grp_split, brows, int(D), p.grp_pad, dHb, s));
+      }
       kd::DwArgs wa{G, H + group_row0 * D, grows, int(D), int(V), p.Vp, dW};
       KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
       gj = 0;

@@ -65,8 +65,9 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
   p.npt = p.c_pad / kTile;
   p.dh_split = dh_split_for(c, D);
   p.dw_group = dw_group_for(c, N);
-  p.grp_pad = ceil_div(p.dw_group * c, kTile) * kTile;
-  p.grp_split = dh_split_for(p.dw_group * c, D);
+  const int64_t dh_rows = p.dw_group * c < kDhRows ? p.dw_group * c : kDhRows;
+  p.grp_pad = ceil_div(dh_rows, kTile) * kTile;
+  p.grp_split = dh_split_for(dh_rows, D);
   // every GEMM operand is addressed with 32-bit buffer offsets (bf16)
   if (p.dw_group * c * p.Vp > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
   if (p.dw_group * c * D > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
@@ -97,7 +98,7 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
   off = shared_end;
   // G rows of a group of dw_group consecutive chunks, in position order
   p.off_g = take(size_t(p.dw_group) * c * p.Vp * 2);
-  // fp32 split-K partials of a group's dH GEMM
+  // fp32 split-K partials of one dH GEMM
   p.off_dhp = take(p.grp_split > 1 ? size_t(p.grp_split) * p.grp_pad * D * 4 : 0);
   const size_t bwd_end = off;
   p.bytes = fwd_end > bwd_end ? fwd_end : bwd_end;

@@ -26,8 +26,8 @@ struct Plan {
   int64_t npt = 0;     // position tiles per chunk
   int dh_split = 1;    // split-K factor of a dH GEMM over one chunk (the kept-gradient comparator)
   int dw_group = 1;    // consecutive chunks whose G rows feed one dW GEMM (K = dw_group * chunk)
-  int64_t grp_pad = 0; // dw_group * chunk rounded up to kTile: rows of a group's dH GEMM
-  int grp_split = 1;   // split-K factor of the dH GEMM over a group
+  int64_t grp_pad = 0; // rows of one dH GEMM over a group: min(group rows, kDhRows), rounded up to kTile
+  int grp_split = 1;   // split-K factor of such a dH GEMM
   // workspace byte offsets
   size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0, off_scalar = 0;  // shared by fwd and bwd
   size_t off_pm = 0, off_ps = 0, off_zsel = 0, off_rowkl = 0;  // forward only
@@ -79,6 +79,11 @@ constexpr int64_t kDwMinK = KD_DW_MIN_K;
 #endif
 constexpr int kMaxDwGroup = KD_MAX_DW_GROUP;
 int dw_group_for(int64_t c, int64_t N);
+
+// Rows per dH GEMM within a group: one round of 256 x 256 tiles at D = 4096
+// (a group of 8192 rows in one GEMM streams each XCD's G strips twice, and
+// measured slower).
+constexpr int64_t kDhRows = 4096;
 
 // Pointer checks shared by the entry points.
 bool aligned(const void* p, size_t a);
