@@ -75,6 +75,21 @@ def test_chunk_independence():
     assert rel(a["dH"], b["dH"]) <= 1e-2 and rel(a["dW"], b["dW"]) <= 1e-4
 
 
+@pytest.mark.parametrize("N,chunk", [(2600, 128), (9000, 1024)])
+def test_group_boundaries(N, chunk):
+    """The backward keeps the G rows of up to 8 chunks (8192 positions) for one
+    dW GEMM and runs dH over them in blocks of at most 4096 rows.  (2600, 128):
+    three groups of 8 chunks, the last one ragged down to a 40-row chunk;
+    (9000, 1024): a full group whose dH runs as two 4096-row blocks, then a
+    ragged 808-row group."""
+    cfg = KDConfig("groups", N=N, D=64, V=3000, K=16, chunk=chunk, ids="uniform", cfg_id=13)
+    say(f"case group boundaries: N={N} chunk={chunk}")
+    inp = _case(cfg)
+    assert_parity(run_gpu(inp, 1.0, chunk, grad_loss=0.6),
+                  O.forward_backward_blocked(inp["H"], inp["W"], inp["idx"], inp["t"], 1.0, block=chunk,
+                                             grad_loss=0.6), what=f"groups N={N} chunk={chunk}")
+
+
 def test_deterministic_bitwise():
     cfg = KDConfig("det", N=600, D=256, V=3000, K=20, chunk=256, cfg_id=14)
     inp = _case(cfg)
