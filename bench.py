@@ -27,7 +27,8 @@ METRIC = "fused top-K KL fwd+bwd tokens/s and % bf16 MFMA peak; peak HBM GiB"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 2516.6
 GEMM_KERNELS = ("logits_fwd", "logits_bwd", "dh", "dw")
-GROUP_POSITIONS = 8192  # positions per dH / dW GEMM of the library (whole chunks, at most 8)
+GROUP_POSITIONS = 8192  # positions per dW GEMM of the library (whole chunks, at most 8)
+DH_ROWS = 4096          # rows per dH GEMM within such a group
 WORKLOAD_NAMES = {"tiny": "tiny", "toy": "toy_lm_head", "large_vocab": "large_vocab_head",
                   "long": "long_context", "very_long": "very_long_context"}
 # HBM traffic per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, with the
@@ -428,7 +429,8 @@ def keep_compare(args):
 def blas_compare(args):
     """The library's four GEMM kernels beside hipBLASLt (torch.mm) on the same
     shapes of --config: the forward / backward logits GEMM of one chunk
-    (H_c W^T), and the dH (G W) and dW (G^T H) GEMMs of one group of chunks.  The library's
+    (H_c W^T), the dH GEMM of one block of a group (G W) and the dW GEMM of
+    one group of chunks (G^T H).  The library's
     kernels carry their fused epilogues (online log-sum-exp, gradient, fp32
     accumulation into dW); torch.mm writes bf16 and does nothing else.  A
     measurement aid: per-launch averages over --steps fused steps, and the
@@ -470,9 +472,11 @@ def blas_compare(args):
     Hc = H[:c]
     G = torch.randn((rows_dw, V), generator=g, device=dev).to(torch.bfloat16)
     Hg = H[:rows_dw]
+    rows_dh = min(rows_dw, DH_ROWS)
+    Gh = G[:rows_dh]
     shapes = {"logits_fwd": (lambda: torch.mm(Hc, W.t()), 2 * c * D * V),
               "logits_bwd": (lambda: torch.mm(Hc, W.t()), 2 * c * D * V),
-              "dh": (lambda: torch.mm(G, W), 2 * rows_dw * D * V),
+              "dh": (lambda: torch.mm(Gh, W), 2 * rows_dh * D * V),
               "dw": (lambda: torch.mm(G.t(), Hg), 2 * rows_dw * D * V)}
     out = {}
     for k, (fn, flops) in shapes.items():
@@ -495,7 +499,8 @@ def blas_compare(args):
                   "hipblaslt_ms": round(blas_ms, 4), "hipblaslt_tflops": round(flops / blas_ms / 1e9, 1),
                   "gflop": round(flops / 1e9, 1)}
         log(f"{k}: {out[k]}")
-    line = {"mode": "gemm_vs_hipblaslt", "config": {**_config_doc(cfg, args.seed), "dw_rows": rows_dw},
+    line = {"mode": "gemm_vs_hipblaslt", "config": {**_config_doc(cfg, args.seed), "dw_rows": rows_dw,
+                                                   "dh_rows": rows_dh},
             "kernels": out}
     print(json.dumps(line), flush=True)
 
