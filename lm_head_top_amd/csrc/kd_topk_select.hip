@@ -9,8 +9,8 @@
 // id), so "larger key" is exactly "larger logit, or equal logit and lower id"
 // and all keys of a row are distinct.  Keys above the running threshold (the
 // K-th best key kept so far) are appended to an LDS candidate list; when the
-// list passes half its capacity it is sorted (bitonic, in LDS), cut to the K
-// best and the threshold raised.  For random logits a row of 131072 admits a
+// list holds TRIG keys (and at least K) it is sorted (bitonic, in LDS), cut to
+// the K best and the threshold raised.  For random logits a row of 131072 admits a
 // few thousand candidates, so the row is read once and sorted about three
 // times.  The next batch of the row is loaded into registers while the
 // current one is filtered.
@@ -30,9 +30,15 @@ namespace {
 #ifndef KD_TOPK_BATCH
 #define KD_TOPK_BATCH 2048
 #endif
+#ifndef KD_TOPK_TRIG
+#define KD_TOPK_TRIG 512
+#endif
 constexpr int TS = KD_TOPK_THREADS;      // threads per row
 constexpr int PER_IT = KD_TOPK_BATCH;    // logits per batch
 constexpr int CAP = 2 * PER_IT;          // candidate keys in LDS (32 KiB at 2048: 4 rows per CU)
+// The list is compacted (and the threshold raised) once it holds TRIG keys,
+// so the threshold follows the running K-th best closely; at most CAP - PER_IT.
+constexpr int TRIG = KD_TOPK_TRIG < CAP - PER_IT ? KD_TOPK_TRIG : CAP - PER_IT;
 static_assert(CAP >= 2 * PER_IT && CAP - PER_IT >= 256, "a batch must fit beside a full list");
 static_assert(PER_IT % (TS * 8) == 0, "a batch is whole 16-byte loads of bf16 for every thread");
 
@@ -51,6 +57,14 @@ __device__ __forceinline__ uint64_t make_key(float x, uint32_t id) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Smallest float that can still carry a key above thr: every key above thr
+// has sortable(x) >= its high word, i.e. x >= this value (-0.0 and +0.0 alike).
+// Below sortable(-inf) lie only NaN patterns; then every non-NaN float passes.
+__device__ __forceinline__ float key_floor(uint64_t thr) {
+  const uint32_t hi = uint32_t(thr >> 32);
+  return hi <= sortable(-INFINITY) ? -INFINITY : unsortable(hi);
+}
 
 // Appends the keys above thr (one wave-aggregated LDS atomic per wave).
 __device__ __forceinline__ void append(uint64_t key, bool valid, uint64_t thr, uint64_t* cand, int* cnt,
@@ -144,7 +158,30 @@ __global__ __launch_bounds__(TS) void topk_select_kernel(const void* __restrict_
       }
     }
   };
+  // Most logits cannot beat the threshold: each is first compared as a float
+  // against key_floor(thr) (a superset of the exact test), one ballot drops a
+  // batch for the whole wave, and the 64-bit key, the exact test and the
+  // append run only for slots where some lane passes.
+  float thr_f = -INFINITY;
   auto filter = [&](int64_t e0, const Reg (&r)[NL]) {
+    bool any = false;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      if constexpr (VEC) {
+        const int64_t e = e0 + int64_t(u * TS + tid) * EPL;  // the row holds whole 16-byte chunks
+        const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) {
+          const float x = DT == 0 ? __uint_as_float(w[q]) : bf16_to_f32((w[q / 2] >> (16 * (q & 1))) & 0xffffu);
+          any |= e < V && x >= thr_f;
+        }
+      } else {
+        const int64_t e = e0 + u * TS + tid;
+        const float x = DT == 0 ? __uint_as_float(r[u]) : bf16_to_f32(r[u]);
+        any |= e < V && x >= thr_f;
+      }
+    }
+    if (__ballot(any) == 0) return;
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       if constexpr (VEC) {
@@ -152,17 +189,17 @@ __global__ __launch_bounds__(TS) void topk_select_kernel(const void* __restrict_
         const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
 #pragma unroll
         for (int q = 0; q < EPL; ++q) {
-          float x;
-          if constexpr (DT == 0)
-            x = __uint_as_float(w[q]);
-          else
-            x = bf16_to_f32((w[q / 2] >> (16 * (q & 1))) & 0xffffu);
-          append(make_key(x, uint32_t(e + q)), e + q < V, thr, cand, &cnt, lane);
+          const float x = DT == 0 ? __uint_as_float(w[q]) : bf16_to_f32((w[q / 2] >> (16 * (q & 1))) & 0xffffu);
+          const bool pass = e < V && x >= thr_f;
+          if (__ballot(pass) == 0) continue;
+          append(make_key(x, uint32_t(e + q)), pass, thr, cand, &cnt, lane);
         }
       } else {
         const int64_t e = e0 + u * TS + tid;
         const float x = DT == 0 ? __uint_as_float(r[u]) : bf16_to_f32(r[u]);
-        append(make_key(x, uint32_t(e)), e < V, thr, cand, &cnt, lane);
+        const bool pass = e < V && x >= thr_f;
+        if (__ballot(pass) == 0) continue;
+        append(make_key(x, uint32_t(e)), pass, thr, cand, &cnt, lane);
       }
     }
   };
@@ -178,9 +215,10 @@ __global__ __launch_bounds__(TS) void topk_select_kernel(const void* __restrict_
     __syncthreads();
     n = cnt;
     __syncthreads();  // every thread has the same n before any thread appends again
-    if (n >= CAP - PER_IT) {
+    if (n >= TRIG && n >= K) {
       n = compact(cand, n, K);
-      thr = cand[K - 1];  // at least CAP - PER_IT >= K keys were admitted, so n == K
+      thr = cand[K - 1];  // n >= K keys were admitted, so n == K now
+      thr_f = key_floor(thr);
       if (tid == 0) cnt = n;
       __syncthreads();
     }
