@@ -272,3 +272,36 @@ def test_invalid_ids_are_memory_safe():
     # rows without bad ids are still right
     ref = O.rows_forward(inp["H"], inp["W"], inp["idx"], inp["t"], [0, 1, 20], cfg.N, 1.0)
     assert np.allclose(lse.double().cpu().numpy()[[0, 1, 20]], ref["lse"], rtol=1e-4)
+
+
+def test_concurrent_streams_with_distinct_workspaces():
+    """Two problems on two streams at once (default priority), each with its
+    own workspace: results bitwise equal to each problem run alone."""
+    import torch
+    import lm_head_top_amd as kd
+    cfgs = [KDConfig("s1", N=1500, D=256, V=9000, K=32, chunk=512, ids="uniform", cfg_id=21),
+            KDConfig("s2", N=900, D=192, V=7000, K=20, chunk=256, ids="uniform", cfg_id=22)]
+    say("case concurrent streams")
+    tens = [to_device(make_inputs(c, 1)) for c in cfgs]
+
+    def run(i, ws):
+        H, W, idx, t = tens[i]
+        c = cfgs[i]
+        loss, lse = kd.forward(H, W, idx, t, 1.0, c.chunk, workspace=ws)
+        dH, dW = kd.backward(H, W, idx, t, lse, None, 1.0, c.chunk, workspace=ws)
+        return loss, lse, dH, dW
+
+    wss = [torch.empty(kd.workspace_size(c.N, c.D, c.V, c.K, c.chunk), dtype=torch.uint8, device="cuda")
+           for c in cfgs]
+    alone = [run(i, wss[i]) for i in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    together = [None, None]
+    for _ in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                together[i] = run(i, wss[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            for a, b in zip(alone[i], together[i]):
+                assert torch.equal(a, b)
