@@ -73,11 +73,25 @@ def cpu_baseline(inp, cfg, rows):
                       f"row-blocked, block={min(cfg.chunk, rows)}); {dt:.1f} s wall"}
 
 
-def source_hash() -> str:
+def code_text(src: str) -> str:
+    """C/C++ source without comments and with whitespace collapsed: edits to
+    comments do not change the code the counters were taken on (the sources
+    hold no comment markers inside string literals)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def source_hash(read=None) -> str:
+    """SHA-256 of the kernel sources' code (comments and layout excluded)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel)) as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(rel.encode() + b"\0" + code_text(text).encode())
     return h.hexdigest()
 
 

@@ -93,15 +93,15 @@ struct CombineArgs {
 };
 
 struct DhArgs {
-  const uint16_t* G;   // [rows, Vp], offset to the chunk's first row
+  const uint16_t* G;   // [rows, Vp], offset to the block's first row
   const uint16_t* W;   // [V, D]
   int rows, D, V;
   int64_t Vp;
   int split;           // number of K splits
   int ktiles_per_split;
   float* part;         // [split, c_pad, D] (split > 1)
-  uint16_t* dH;        // [rows, D] offset to the chunk (split == 1)
-  int64_t c_pad;
+  uint16_t* dH;        // [rows, D] offset to the block (split == 1)
+  int64_t c_pad;       // row stride of `part` per split (the block's rows, padded)
   const float* scale;  // device scalar multiplying the result, or null
 };
 

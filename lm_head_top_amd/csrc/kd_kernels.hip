@@ -17,15 +17,17 @@
 //             backward: G = g/(N T) (exp(z - lse) - p scattered at the ids),
 //                      rounded to bf16 into G_c[c, V];
 //   combine   forward: merge the vocab-tile partials into lse and KL per row;
-//   dh / dw   dH_c = G_c W (split over V, fp32 partials) and dW += G^T H over a
-//             group of chunks, reading G, W and H as they are stored.
+//   dh / dw   over the G rows of a group of chunks: dH = G W in blocks of up to
+//             4096 rows (split over V into fp32 partials only when a block's
+//             tiles cannot fill the chip) and dW += G^T H, reading G, W and H
+//             as they are stored.
 //
 // GEMM core: a 256 x 256 output tile per workgroup, split over waves 2 (M) x
 // WAVES/2 (N); each wave holds its (128 x 256/(WAVES/2)) part as 32x32 fp32
 // MFMA accumulators.  Tiles of BK along K stream from HBM straight into LDS
 // with buffer_load_dwordx4 ... lds (no register staging; out-of-range rows
 // and columns read as zero), through a ring of STAGES buffers.  An operand
-// is either K-contiguous (W and H_c in the logits GEMM, G_c in dH): its LDS
+// is either K-contiguous (W and H_c in the logits GEMM, G in dH): its LDS
 // tile is 256 rows of BK, 16-byte chunks XOR-swizzled by row, and a fragment
 // is one ds_read_b128; or k-major (W in dH, G and H in dW): its LDS tile is
 // BK rows of 256, 64-byte blocks XOR-swizzled by row, and a fragment is two
@@ -1040,7 +1042,7 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
   if (k_end > a.Vp) k_end = int(a.Vp);
   f32x16 acc[MI][NJ];
   {
-    // A = G_c (positions x vocab, vocab-contiguous); B = W read k-major
+    // A = G (positions x vocab, vocab-contiguous); B = W read k-major
     // (vocab rows, D contiguous) through the transposing fragment reads
     DLoad la;
     MLoad lb;

@@ -22,7 +22,7 @@ struct Plan {
   float T = 1.f;
   int64_t c_pad = 0;   // chunk rounded up to kTile
   int64_t nvt = 0;     // vocab tiles
-  int64_t Vp = 0;      // V rounded up to kTile (row stride of G_c)
+  int64_t Vp = 0;      // V rounded up to kTile (row stride of G)
   int64_t npt = 0;     // position tiles per chunk
   int dh_split = 1;    // split-K factor of a dH GEMM over one chunk (the kept-gradient comparator)
   int dw_group = 1;    // consecutive chunks whose G rows feed one dW GEMM (K = dw_group * chunk)

@@ -95,3 +95,14 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_source_hash_ignores_comments_not_code():
+    import bench
+    a = "int f(int x) {\n  return x + 1;  // one more\n}\n/* block\n comment */\n"
+    b = "int f(int x) {\n    return x + 1;\n}\n"
+    c = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert bench.source_hash() == bench.source_hash(
+        lambda rel: open(os.path.join(ROOT, rel)).read() + "\n// a trailing comment\n")
