@@ -637,8 +637,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="toy", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=512,
-                    help="positions of the CPU-oracle sample (0 skips it)")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="positions of the CPU-oracle sample, about 10 s of fp64 work on 16 "
+                         "host threads at the toy head (0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain fp32 copy of this many MiB before warmup, as the known "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE")
