@@ -73,8 +73,13 @@ typedef enum kd_status {
  * arguments, never on the device.  Returns 0 for arguments that the entry
  * points would reject.  The workspace holds one chunk's teacher
  * probabilities and id buckets, the forward's per-vocab-tile softmax
- * partials, one chunk's bf16 gradient G_c[chunk, V] and dH split partials:
- * O(chunk * (V + K + D)) bytes plus 4 N bytes -- never O(N * V).
+ * partials and, for the backward, the bf16 gradient rows G of one group of
+ * consecutive chunks (the fewest whole chunks that hold 8192 positions, at
+ * most 8 chunks and at most N positions) with fp32 split partials for dH
+ * when a block of rows is too small to fill the device.  The size is
+ * O(R * V + chunk * K) bytes plus 4 N bytes, where R is the
+ * group's rows (at most max(chunk, 8192) rounded to whole chunks): bounded
+ * in N, never O(N * V).
  */
 size_t kd_topk_kl_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K,
                                  int64_t chunk);
