@@ -173,6 +173,24 @@ def test_forward_gather_at_edge_ids():
     assert_parity(g, ref, what="gather-edges")
 
 
+def test_max_vocabulary():
+    """V = KD_MAX_V, the largest vocabulary accepted: 4096 vocab tiles, so the
+    bucketing runs with its fewest counters per tile, and ids reach the last
+    tile.  Two chunks, the second ragged; fp64 oracle row-blocked by chunk."""
+    N, D, K, chunk = 300, 64, 40, 256
+    V = 1 << 20
+    say(f"case max vocabulary N={N} D={D} V={V} K={K} chunk={chunk}")
+    idx, _ = _edge_ids(V, K, N, 21)
+    r = np.random.default_rng(22)
+    H = f32_to_bf16_bits(r.standard_normal((N, D)).astype(np.float32))
+    W = f32_to_bf16_bits((r.standard_normal((V, D)) / math.sqrt(D)).astype(np.float32))
+    t = -np.sort(-r.standard_normal((N, K)).astype(np.float32) * math.sqrt(3), axis=1)
+    inp = {"H": H, "W": W, "idx": idx, "t": t}
+    g = run_gpu(inp, 1.0, chunk)
+    ref = O.forward_backward_blocked(H, W, idx, t, 1.0, block=chunk)
+    assert_parity(g, ref, what="V=KD_MAX_V")
+
+
 def test_k1_and_k_equals_v():
     cfg = KDConfig("k1", N=130, D=64, V=1000, K=1, chunk=64, ids="uniform", cfg_id=15)
     inp = _case(cfg)

@@ -95,6 +95,15 @@ def test_special_values_and_limits():
     _check(r.standard_normal((3, 20000)).astype(np.float32) - 1e3, 100)  # all negative
 
 
+def test_very_long_rows():
+    """Rows of 2^21 logits (16 times the toy vocabulary): many load batches
+    and compactions per row, fp32 and bf16 (with a ragged tail)."""
+    say("case topk very long rows")
+    r = np.random.default_rng(6)
+    _check(r.standard_normal((3, 1 << 21)).astype(np.float32), 256)
+    _check(_bf16(r.standard_normal((2, (1 << 21) + 3))), 100, bf16=True)
+
+
 def test_empty_batch():
     import torch
     import lm_head_top_amd as kd
