@@ -57,6 +57,14 @@ def test_temperature_and_grad_scale():
                   what="T=2")
 
 
+def test_low_temperature():
+    """T = 0.25 sharpens both distributions (student logits up to ~16 in
+    magnitude, teacher mass on few ids)."""
+    cfg = get_config("tiny").replace(name="tiny_T025", T=0.25, cfg_id=24)
+    inp = _case(cfg)
+    assert_parity(run_gpu(inp, 0.25, cfg.chunk), _oracle(inp, 0.25), what="T=0.25")
+
+
 def test_chunk_larger_than_N_and_not_tile_multiple():
     cfg = KDConfig("clamp", N=300, D=64, V=1000, K=9, chunk=100000, ids="uniform", cfg_id=13)
     inp = _case(cfg)
@@ -204,6 +212,20 @@ def test_max_k():
     cfg = KDConfig("kmax", N=100, D=64, V=3000, K=256, chunk=64, ids="uniform", cfg_id=17)
     inp = _case(cfg)
     assert_parity(run_gpu(inp, 1.0, cfg.chunk), _oracle(inp, 1.0), what="K=256")
+
+
+def test_minus_inf_teacher_logits():
+    """Cache entries with teacher logit -inf (a masked token) get p = 0 and
+    add nothing (0 log 0 = 0); rows with a single finite entry put all their
+    mass on one id."""
+    cfg = KDConfig("neginf", N=200, D=64, V=3000, K=32, chunk=64, ids="uniform", cfg_id=23)
+    inp = _case(cfg)
+    inp["t"][0::2, 20:] = -np.inf
+    inp["t"][1::4, 1:] = -np.inf
+    g = run_gpu(inp, 1.0, cfg.chunk)
+    ref = _oracle(inp, 1.0)
+    assert np.all(np.isfinite(g["row_kl"]))
+    assert_parity(g, ref, what="-inf teacher logits")
 
 
 def test_duplicate_ids_scatter_add():
