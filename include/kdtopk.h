@@ -41,6 +41,9 @@
  *   - Token ids outside [0, V) give unspecified (but memory-safe) results;
  *     kd_topk_kl_validate detects them.  Duplicate ids within a row act as
  *     one entry holding the summed probability.
+ *   - A teacher logit of -inf gives its entry p = 0 (a masked token).  A row
+ *     whose K teacher logits are all -inf has no teacher distribution; its
+ *     results are unspecified.
  *   - Calls on different streams need distinct workspaces; forward and
  *     backward may share one workspace when issued in order on one stream.
  *   - Results are deterministic: the same inputs give bit-identical outputs
