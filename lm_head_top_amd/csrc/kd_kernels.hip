@@ -105,12 +105,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 -> bf16, round to nearest even, by gfx950's v_cvt_pk_bf16_f32 (two
+// values per instruction; denormals kept, NaN stays a NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -670,17 +673,29 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
   const uint32_t* ent = CACHE ? a.ent + int64_t(pt) * kTile * a.KE : nullptr;
 
   if (MODE == 0 || MODE == 2 || MODE == 3) {
-    // z = acc / T; vocab rows past V do not exist
+    // vocab rows past V do not exist (a uniform branch: only the last vocab tile)
+    if (vtail) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float z = acc[i][j][r] * a.invT;
-          if (vtail && v0 + acc_row(wm, i, r, lane) >= a.V) z = -INFINITY;
-          acc[i][j][r] = z;
-        }
+          for (int r = 0; r < 16; ++r)
+            if (v0 + acc_row(wm, i, r, lane) >= a.V) acc[i][j][r] = -INFINITY;
+    }
+    // the top-K mode keeps acc = T z (T > 0, so the order and the max carry
+    // over) and folds 1/T into the exponent and the gathered values; the
+    // others need z = acc / T in the registers
+    constexpr bool SCALED = MODE != 0;
+    if (SCALED) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= a.invT;
+    }
+    const float ez = SCALED ? LOG2E : a.invT * LOG2E;  // exp(z - m) = exp2(acc ez - m_acc ez)
     if (MODE == 2) {
       // keep z[position][vocab] (fp32, row stride Vp): registers 4g .. 4g+3
       // of a block are 4 consecutive vocab rows at one position
@@ -708,12 +723,13 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
         for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
       float s = 0.f;
       if (m != -INFINITY) {
-        const float mb = m * LOG2E;
+        const float mb = m * ez;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s += exp2_fast(fmaf(acc[i][j][r], LOG2E, -mb));
+          for (int r = 0; r < 16; ++r) s += exp2_fast(fmaf(acc[i][j][r], ez, -mb));
       }
+      if (!SCALED) m *= a.invT;  // the max in logit units
       lse_merge(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32));
       if (lane < 32) {
         const int pl = acc_col(wn, j, lane);
@@ -796,7 +812,8 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
         const int row = int(pk >> 17);
         if ((row >> 7) == h) {
           const int vl = int((pk >> 9) & 0xffu), k = int(pk & 0x1ffu);
-          a.zsel[int64_t(p0 + row) * a.KE + k] = S[(row & 127) * SLD + vl];
+          const float zv = S[(row & 127) * SLD + vl];
+          a.zsel[int64_t(p0 + row) * a.KE + k] = SCALED ? zv : zv * a.invT;
         }
       }
       __syncthreads();
@@ -815,17 +832,25 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
       const bool lab = ok && a.labels != nullptr && unsigned(a.labels[prow]) < unsigned(a.V);
       qs[j] = gs * rs * (lab ? a.alpha + a.beta : a.alpha);
     }
-    // gs * softmax(z) over the full vocabulary, from the forward's lse
+    // gs * softmax(z) over the full vocabulary, from the forward's lse:
+    // exp(acc / T - lse) = exp2(acc ez - lse log2 e)
+    const float ez = a.invT * LOG2E;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float q = exp2_fast(fmaf(acc[i][j][r] * a.invT, LOG2E, -lse_l2[j]));
-          if (vtail && v0 + acc_row(wm, i, r, lane) >= a.V) q = 0.f;
-          acc[i][j][r] = qs[j] * q;
-        }
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = qs[j] * exp2_fast(fmaf(acc[i][j][r], ez, -lse_l2[j]));
+    // vocab rows past V do not exist (a uniform branch: only the last vocab tile)
+    if (vtail) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (v0 + acc_row(wm, i, r, lane) >= a.V) acc[i][j][r] = 0.f;
+    }
     if (MODE == 4) {
       // minus gs * softmax(t / T) over the full vocabulary, from the teacher's lse
 #pragma unroll
@@ -877,10 +902,10 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
           const float4 x0 = *reinterpret_cast<const float4*>(S + pl * SLD + c8);
           const float4 x1 = *reinterpret_cast<const float4*>(S + pl * SLD + c8 + 4);
           uint4 o;
-          o.x = bf16_rne(x0.x) | (bf16_rne(x0.y) << 16);
-          o.y = bf16_rne(x0.z) | (bf16_rne(x0.w) << 16);
-          o.z = bf16_rne(x1.x) | (bf16_rne(x1.y) << 16);
-          o.w = bf16_rne(x1.z) | (bf16_rne(x1.w) << 16);
+          o.x = bf16x2_rne(x0.x, x0.y);
+          o.y = bf16x2_rne(x0.z, x0.w);
+          o.z = bf16x2_rne(x1.x, x1.y);
+          o.w = bf16x2_rne(x1.z, x1.w);
           *reinterpret_cast<uint4*>(a.G + int64_t(prow) * a.Vp + v0 + c8) = o;
         }
       }
@@ -1088,8 +1113,8 @@ __global__ __launch_bounds__(NT) void dh_reduce_kernel(const float* __restrict__
     s.w += x.w;
   }
   uint2 o;
-  o.x = bf16_rne(s.x) | (bf16_rne(s.y) << 16);
-  o.y = bf16_rne(s.z) | (bf16_rne(s.w) << 16);
+  o.x = bf16x2_rne(s.x, s.y);
+  o.y = bf16x2_rne(s.z, s.w);
   reinterpret_cast<uint2*>(dH)[i] = o;
 }
 
@@ -1168,10 +1193,10 @@ __global__ __launch_bounds__(NT) void keep_convert_kernel(const float* __restric
   const float4 x0 = reinterpret_cast<const float4*>(z)[2 * q];
   const float4 x1 = reinterpret_cast<const float4*>(z)[2 * q + 1];
   uint4 o;
-  o.x = bf16_rne(gs * x0.x) | (bf16_rne(gs * x0.y) << 16);
-  o.y = bf16_rne(gs * x0.z) | (bf16_rne(gs * x0.w) << 16);
-  o.z = bf16_rne(gs * x1.x) | (bf16_rne(gs * x1.y) << 16);
-  o.w = bf16_rne(gs * x1.z) | (bf16_rne(gs * x1.w) << 16);
+  o.x = bf16x2_rne(gs * x0.x, gs * x0.y);
+  o.y = bf16x2_rne(gs * x0.z, gs * x0.w);
+  o.z = bf16x2_rne(gs * x1.x, gs * x1.y);
+  o.w = bf16x2_rne(gs * x1.z, gs * x1.w);
   reinterpret_cast<uint4*>(G)[q] = o;
 }
 
