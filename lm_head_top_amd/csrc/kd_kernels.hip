@@ -58,6 +58,17 @@
 #ifndef KD_LOAD_AUX
 #define KD_LOAD_AUX 0
 #endif
+// Operand given a third LDS slot, so its loads run two stages ahead:
+// 0 none, 1 A, 2 B (per GEMM kernel; two-slot rings only)
+#ifndef KD_DEEP_LOGITS
+#define KD_DEEP_LOGITS 1
+#endif
+#ifndef KD_DEEP_DH
+#define KD_DEEP_DH 0
+#endif
+#ifndef KD_DEEP_DW
+#define KD_DEEP_DW 0
+#endif
 
 namespace kd {
 namespace {
@@ -80,12 +91,15 @@ constexpr int NI = kTile * ROWB / 1024 / WAVES;  // direct loads per wave, per o
 constexpr int OPER_BYTES = kTile * ROWB;         // one operand tile in LDS
 constexpr int STAGE_BYTES = 2 * OPER_BYTES;
 constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
+// LDS of the main loop when one operand has a third slot
+constexpr int ring_bytes(int deep) { return deep ? MAIN_BYTES + OPER_BYTES : MAIN_BYTES; }
 constexpr int NS = BK / 16;                      // 16-deep MFMA steps per stage
 constexpr int LPS = KD_LPS;                      // ring loads issued per MFMA step (front-loaded)
 constexpr int SLD = kTile + 4;                   // fp32 row stride of the epilogue staging tile
 constexpr int STAGE_FLOATS = 128 * SLD;          // half a tile: 128 positions x 256 vocab
 constexpr int EPI_BYTES = (STAGE_FLOATS + 10 * kTile) * 4;
-constexpr int SMEM_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+constexpr int SMEM_BYTES =
+    ring_bytes(KD_DEEP_LOGITS) > EPI_BYTES ? ring_bytes(KD_DEEP_LOGITS) : EPI_BYTES;
 constexpr uint32_t kOOB = 0xFFFFFFF0u;           // buffer offset past any operand: reads return 0
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -93,7 +107,8 @@ static_assert(BK == 32 || BK == 64, "BK");
 static_assert(WAVES == 4 || WAVES == 8, "WAVES");
 static_assert(LPS > 0 && LPS <= MI * NJ && (2 * NI) % LPS == 0 && 2 * NI <= LPS * NS, "LPS");
 static_assert(STAGES >= 2, "STAGES");
-static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+static_assert(SMEM_BYTES <= 160 * 1024 && ring_bytes(1) <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+static_assert(STAGES == 2 || (KD_DEEP_LOGITS == 0 && KD_DEEP_DH == 0 && KD_DEEP_DW == 0), "deep slot");
 
 // GEMM kernels: one workgroup per compute unit; with 4 waves each wave may use
 // the whole register file of its SIMD (accumulators in AGPRs).
@@ -288,11 +303,11 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* tile, int col0, int s, int
 // Fragments of the next 16-deep step load while the current step multiplies,
 // and the next stage's ring loads (2 * NI per wave) go out LPS per step, each
 // between two MFMAs.
-template <bool AMN, bool BMN, class LA, class LB>
+template <bool AMN, bool BMN, bool B_FIRST, class LA, class LB>
 __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const char* __restrict__ sB,
                                           f32x16 (&acc)[MI][NJ], int wm, int wn, int lane,
-                                          const LA& la, const LB& lb, char* nst, int nk0,
-                                          int ka_lim, int kb_lim) {
+                                          const LA& la, const LB& lb, char* nA, int nka, char* nB,
+                                          int nkb, int ka_lim, int kb_lim) {
   constexpr int NR = (AMN ? 2 : 1) * MI + (BMN ? 2 : 1) * NJ;  // fragment reads per step
   constexpr int NQ = MI * NJ;                                  // MFMAs per step
   const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31);   // K-contiguous tile rows are r31 mod 32
@@ -327,10 +342,14 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
 #pragma unroll
     for (int q = 0; q < LPS; ++q) {
       const int l = l0 + q;
-      if (l < NI)
-        la.issue_one(l, nst, nk0, ka_lim);
-      else if (l < NL)
-        lb.issue_one(l - NI, nst + OPER_BYTES, nk0, kb_lim);
+      // the operand loaded first is the one that must land by the next stage
+      if (l < NI) {
+        if (B_FIRST) lb.issue_one(l, nB, nkb, kb_lim);
+        else la.issue_one(l, nA, nka, ka_lim);
+      } else if (l < NL) {
+        if (B_FIRST) la.issue_one(l - NI, nA, nka, ka_lim);
+        else lb.issue_one(l - NI, nB, nkb, kb_lim);
+      }
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -356,9 +375,21 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
 
 // acc[i][j] (wave (wm, wn) = (wave / WAVES_N, wave % WAVES_N)) register r holds C[m][n] with
 //   m = wm*WT_M + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*WT_N + j*32 + lane%32.
-template <bool AMN = false, bool BMN = false, class LA, class LB>
+// DEEP = 1 (2): operand A (B) has three LDS slots and its loads run two
+// stages ahead; the other operand's loads go out first in each stage, so one
+// vmcnt wait that leaves only the deep operand's newest loads in flight
+// covers both operands of the current stage.  LDS holds the A slots, then the
+// B slots, OPER_BYTES each (ring_bytes(DEEP) in all).
+template <bool AMN = false, bool BMN = false, int DEEP = 0, class LA, class LB>
 __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int k_begin, int k_end,
                                           int ka_lim, int kb_lim, f32x16 (&acc)[MI][NJ], char* smem) {
+  static_assert(DEEP >= 0 && DEEP <= 2 && (DEEP == 0 || STAGES == 2), "DEEP");
+  constexpr int SA = STAGES + (DEEP == 1 ? 1 : 0);  // A slots
+  constexpr int SB = STAGES + (DEEP == 2 ? 1 : 0);  // B slots
+  constexpr int AHEAD_A = SA - 1, AHEAD_B = SB - 1;  // stages each operand loads ahead
+  constexpr bool B_FIRST = DEEP == 1;
+  char* const sa0 = smem;
+  char* const sb0 = smem + SA * OPER_BYTES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 #pragma unroll
@@ -369,24 +400,36 @@ __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int k_begi
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (k_end - k_begin + BK - 1) / BK;
   if (nk <= 0) return;
+  // stages past the end read as zero
+  if (DEEP == 0) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {  // stages past the end read as zero
-    char* st = smem + s * STAGE_BYTES;
-    la.issue(st, k_begin + s * BK, ka_lim);
-    lb.issue(st + OPER_BYTES, k_begin + s * BK, kb_lim);
+    for (int s = 0; s < STAGES - 1; ++s) {
+      la.issue(sa0 + s * OPER_BYTES, k_begin + s * BK, ka_lim);
+      lb.issue(sb0 + s * OPER_BYTES, k_begin + s * BK, kb_lim);
+    }
+  } else if (DEEP == 1) {
+    la.issue(sa0, k_begin, ka_lim);
+    lb.issue(sb0, k_begin, kb_lim);
+    la.issue(sa0 + OPER_BYTES, k_begin + BK, ka_lim);
+  } else {
+    lb.issue(sb0, k_begin, kb_lim);
+    la.issue(sa0, k_begin, ka_lim);
+    lb.issue(sb0 + OPER_BYTES, k_begin + BK, kb_lim);
   }
   for (int kt = 0; kt < nk; ++kt) {
-    // every iteration issues one stage's loads, so once only the newer
-    // STAGES - 2 stages' loads may be in flight, stage kt has landed
-    wait_vmcnt<(STAGES - 2) * 2 * NI>();
+    // every iteration issues one stage of each operand; once only the newer
+    // loads allowed in flight remain, stage kt of both operands has landed
+    if (DEEP == 0) wait_vmcnt<(STAGES - 2) * 2 * NI>();
+    else wait_vmcnt<NI>();
     lds_barrier();
-    // the next stage refills the buffer every wave finished reading last
-    // iteration; near the end it loads zeros that nothing reads
-    const int nxt = kt + STAGES - 1;
-    const int nk0 = nxt < nk ? k_begin + nxt * BK : 0x3fffffff;
-    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    mma_stage<AMN, BMN>(st, st + OPER_BYTES, acc, wm, wn, lane, la, lb, smem + (nxt % STAGES) * STAGE_BYTES,
-                        nk0, ka_lim, kb_lim);
+    // the next loads refill the slots every wave finished reading last
+    // iteration; near the end they load zeros that nothing reads
+    const int na = kt + AHEAD_A, nb = kt + AHEAD_B;
+    const int nka = na < nk ? k_begin + na * BK : 0x3fffffff;
+    const int nkb = nb < nk ? k_begin + nb * BK : 0x3fffffff;
+    mma_stage<AMN, BMN, B_FIRST>(sa0 + (kt % SA) * OPER_BYTES, sb0 + (kt % SB) * OPER_BYTES, acc, wm, wn, lane,
+                                 la, lb, sa0 + (na % SA) * OPER_BYTES, nka, sb0 + (nb % SB) * OPER_BYTES, nkb,
+                                 ka_lim, kb_lim);
   }
   wait_vmcnt<0>();  // the trailing zero loads land before the epilogue reuses LDS
   lds_barrier();
@@ -661,7 +704,7 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
     DLoad la, lb;
     la.init(a.W, uint64_t(a.V) * a.D * 2, a.D, v0, a.V);
     lb.init(a.Hc, uint64_t(a.rows) * a.D * 2, a.D, p0, a.rows);
-    gemm_core(la, lb, 0, a.D, a.D, a.D, acc, smem);
+    gemm_core<false, false, KD_DEEP_LOGITS>(la, lb, 0, a.D, a.D, a.D, acc, smem);
   }
 
   float* S = reinterpret_cast<float*>(smem);
@@ -1051,7 +1094,7 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const float* __restrict__ 
 // --------------------------------------------------------------- dH and dW ---
 
 KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[MAIN_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[ring_bytes(KD_DEEP_DH)];
   const int tiles_m = (a.rows + kTile - 1) / kTile;
   const int tiles_n = (a.D + kTile - 1) / kTile;
   const int tiles = tiles_m * tiles_n;
@@ -1073,7 +1116,7 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
     MLoad lb;
     la.init(a.G, uint64_t(a.rows) * a.Vp * 2, a.Vp, tm * kTile, a.rows);
     lb.init(a.W, uint64_t(a.V) * a.D * 2, a.D, tn * kTile, a.D);
-    gemm_core<false, true>(la, lb, k_begin, k_end, int(a.Vp), a.V, acc, smem);
+    gemm_core<false, true, KD_DEEP_DH>(la, lb, k_begin, k_end, int(a.Vp), a.V, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -1119,7 +1162,7 @@ __global__ __launch_bounds__(NT) void dh_reduce_kernel(const float* __restrict__
 }
 
 KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[MAIN_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[ring_bytes(KD_DEEP_DW)];
   const int tiles_m = int((a.V + kTile - 1) / kTile);
   const int tiles_n = (a.D + kTile - 1) / kTile;
   const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
@@ -1131,7 +1174,7 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
     MLoad la, lb;
     la.init(a.G, uint64_t(a.rows) * a.Vp * 2, a.Vp, tm * kTile, int(a.Vp));
     lb.init(a.H, uint64_t(a.rows) * a.D * 2, a.D, tn * kTile, a.D);
-    gemm_core<true, true>(la, lb, 0, a.rows, a.rows, a.rows, acc, smem);
+    gemm_core<true, true, KD_DEEP_DW>(la, lb, 0, a.rows, a.rows, a.rows, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
