@@ -58,6 +58,18 @@
 #ifndef KD_LOAD_AUX
 #define KD_LOAD_AUX 0
 #endif
+// 1: each stage's barrier sits in its last MFMA step, after that step's
+// fragments are in registers, so the next stage's first fragment reads and
+// the ring refills overlap the step's MFMAs (per GEMM kernel)
+#ifndef KD_EB_LOGITS
+#define KD_EB_LOGITS 0
+#endif
+#ifndef KD_EB_DH
+#define KD_EB_DH 1
+#endif
+#ifndef KD_EB_DW
+#define KD_EB_DW 1
+#endif
 // Operand given a third LDS slot, so its loads run two stages ahead:
 // 0 none, 1 A, 2 B (per GEMM kernel; two-slot rings only)
 #ifndef KD_DEEP_LOGITS
@@ -170,6 +182,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's loads but the newest N have
+// landed and its LDS reads are done.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
 // Workgroup barrier that orders LDS accesses for the compiler but does not wait
 // for outstanding loads (the LDS ring is managed with explicit vmcnt waits).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -212,7 +232,8 @@ struct DLoad {
   // Load j (of NI) of the 256 x BK tile at columns [k0, k0 + BK) into stage.
   __device__ __forceinline__ void issue_one(int j, char* stage, int k0, int k_lim) const {
     const int wave = threadIdx.x >> 6;
-    const uint32_t off = (voff[j] != kOOB && k0 + kc[j] < k_lim) ? voff[j] + uint32_t(k0) * 2u : kOOB;
+    const bool ok = (voff[j] != kOOB) & (k0 + kc[j] < k_lim);
+    const uint32_t off = ok ? voff[j] + uint32_t(k0) * 2u : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * NI + j) * 1024), 16, off,
                                              0, 0, KD_LOAD_AUX);
   }
@@ -255,7 +276,9 @@ struct MLoad {
   // Load j (of NI) of the BK x 256 tile at rows [k0, k0 + BK) into stage.
   __device__ __forceinline__ void issue_one(int j, char* stage, int k0, int k_lim) const {
     const int wave = threadIdx.x >> 6;
-    const uint32_t off = (voff[j] != kOOB && k0 + kr[j] < k_lim) ? voff[j] + uint32_t(k0) * ldb : kOOB;
+    // non-short-circuit test: a select, not a branch around the load
+    const bool ok = (voff[j] != kOOB) & (k0 + kr[j] < k_lim);
+    const uint32_t off = ok ? voff[j] + uint32_t(k0) * ldb : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * NI + j) * 1024), 16, off,
                                              0, 0, KD_LOAD_AUX);
   }
@@ -375,12 +398,97 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
 
 // acc[i][j] (wave (wm, wn) = (wave / WAVES_N, wave % WAVES_N)) register r holds C[m][n] with
 //   m = wm*WT_M + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*WT_N + j*32 + lane%32.
+// One BK-deep stage with the barrier in its last step.  On entry fa[0] and
+// fb[0] hold the stage's first-step fragments; steps read the next step's
+// fragments while they multiply.  In the last step the wave waits for its own
+// loads of the next stage (all but the newest VMW) and for its LDS reads, then
+// passes the workgroup barrier: every wave has then finished reading this
+// stage's slots and the next stage has landed.  It then reads the next
+// stage's first-step fragments from nsA / nsB (into fa[0] / fb[0]) and
+// refills this stage's slots (ring loads to ldA / ldB, the operand that must
+// land first going out first) while the last step's MFMAs run.
+template <bool AMN, bool BMN, bool B_FIRST, int VMW, class LA, class LB>
+__device__ __forceinline__ void mma_stage_eb(const char* __restrict__ sA, const char* __restrict__ sB,
+                                             const char* __restrict__ nsA, const char* __restrict__ nsB,
+                                             bf16x8 (&fa)[2][MI], bf16x8 (&fb)[2][NJ], f32x16 (&acc)[MI][NJ],
+                                             int wm, int wn, int lane, const LA& la, const LB& lb, char* ldA,
+                                             int lka, char* ldB, int lkb, int ka_lim, int kb_lim) {
+  constexpr int NR = (AMN ? 2 : 1) * MI + (BMN ? 2 : 1) * NJ;  // fragment reads per step
+  constexpr int NQ = MI * NJ;                                  // MFMAs per step
+  constexpr int NL = 2 * NI;                                   // ring loads per stage
+  static_assert(NS % 2 == 0, "the next stage's first fragments go to buffer 0");
+  const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31);
+  const int mo = mn_lane_off(lane);
+  auto read_a = [&](const char* t, int i, int st) -> bf16x8 {
+    if constexpr (AMN) return frag_mn(t, wm * WT_M + i * 32, st, lane, mo);
+    else
+      return *reinterpret_cast<const bf16x8*>(t + (wm * WT_M + i * 32 + r31) * ROWB + (((2 * st + hi) ^ sw) * 16));
+  };
+  auto read_b = [&](const char* t, int j, int st) -> bf16x8 {
+    if constexpr (BMN) return frag_mn(t, wn * WT_N + j * 32, st, lane, mo);
+    else
+      return *reinterpret_cast<const bf16x8*>(t + (wn * WT_N + j * 32 + r31) * ROWB + (((2 * st + hi) ^ sw) * 16));
+  };
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+    const int cur = s & 1;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) fa[cur ^ 1][i] = read_a(sA, i, s + 1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb[cur ^ 1][j] = read_b(sB, j, s + 1);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      const int rq = (NR * (q + 1)) / NQ - (NR * q) / NQ;
+#pragma unroll
+      for (int u = 0; u < rq; ++u) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  constexpr int cur = (NS - 1) & 1;
+  wait_vmcnt_lds<VMW>();
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < MI; ++i) fa[cur ^ 1][i] = read_a(nsA, i, 0);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) fb[cur ^ 1][j] = read_b(nsB, j, 0);
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    if (l < NI) {
+      if (B_FIRST) lb.issue_one(l, ldB, lkb, kb_lim);
+      else la.issue_one(l, ldA, lka, ka_lim);
+    } else {
+      if (B_FIRST) la.issue_one(l - NI, ldA, lka, ka_lim);
+      else lb.issue_one(l - NI, ldB, lkb, kb_lim);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    const int rq = (NR * (q + 1)) / NQ - (NR * q) / NQ;
+#pragma unroll
+    for (int u = 0; u < rq; ++u) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    const int lq = (NL * (q + 1)) / NQ - (NL * q) / NQ;
+#pragma unroll
+    for (int u = 0; u < lq; ++u) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
 // DEEP = 1 (2): operand A (B) has three LDS slots and its loads run two
 // stages ahead; the other operand's loads go out first in each stage, so one
 // vmcnt wait that leaves only the deep operand's newest loads in flight
 // covers both operands of the current stage.  LDS holds the A slots, then the
 // B slots, OPER_BYTES each (ring_bytes(DEEP) in all).
-template <bool AMN = false, bool BMN = false, int DEEP = 0, class LA, class LB>
+template <bool AMN = false, bool BMN = false, int DEEP = 0, bool EB = false, class LA, class LB>
 __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int k_begin, int k_end,
                                           int ka_lim, int kb_lim, f32x16 (&acc)[MI][NJ], char* smem) {
   static_assert(DEEP >= 0 && DEEP <= 2 && (DEEP == 0 || STAGES == 2), "DEEP");
@@ -400,6 +508,47 @@ __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int k_begi
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (k_end - k_begin + BK - 1) / BK;
   if (nk <= 0) return;
+  if (EB) {
+    // loads of stage s of an operand go to slot s % slots; stages past the
+    // end read as zero.  Prologue: A0 B0 A1 B1, then A2 (DEEP 1) or B2 (DEEP 2).
+    la.issue(sa0, k_begin, ka_lim);
+    lb.issue(sb0, k_begin, kb_lim);
+    la.issue(sa0 + OPER_BYTES, 1 < nk ? k_begin + BK : 0x3fffffff, ka_lim);
+    lb.issue(sb0 + OPER_BYTES, 1 < nk ? k_begin + BK : 0x3fffffff, kb_lim);
+    if (DEEP == 1) la.issue(sa0 + 2 * OPER_BYTES, 2 < nk ? k_begin + 2 * BK : 0x3fffffff, ka_lim);
+    if (DEEP == 2) lb.issue(sb0 + 2 * OPER_BYTES, 2 < nk ? k_begin + 2 * BK : 0x3fffffff, kb_lim);
+    wait_vmcnt<(DEEP ? 3 : 2) * NI>();  // stage 0 of both operands
+    lds_barrier();
+    bf16x8 fa[2][MI], fb[2][NJ];
+    {
+      const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31), mo = mn_lane_off(lane);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        if constexpr (AMN) fa[0][i] = frag_mn(sa0, wm * WT_M + i * 32, 0, lane, mo);
+        else fa[0][i] = *reinterpret_cast<const bf16x8*>(sa0 + (wm * WT_M + i * 32 + r31) * ROWB + ((hi ^ sw) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if constexpr (BMN) fb[0][j] = frag_mn(sb0, wn * WT_N + j * 32, 0, lane, mo);
+        else fb[0][j] = *reinterpret_cast<const bf16x8*>(sb0 + (wn * WT_N + j * 32 + r31) * ROWB + ((hi ^ sw) * 16));
+      }
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      // after this stage's barrier its slots take stage kt + slots; the
+      // next stage's operands come from slot (kt + 1) % slots
+      const int na = kt + SA, nb = kt + SB;
+      const int lka = na < nk ? k_begin + na * BK : 0x3fffffff;
+      const int lkb = nb < nk ? k_begin + nb * BK : 0x3fffffff;
+      char* const cA = sa0 + (kt % SA) * OPER_BYTES;
+      char* const cB = sb0 + (kt % SB) * OPER_BYTES;
+      mma_stage_eb<AMN, BMN, B_FIRST, DEEP ? NI : 0>(cA, cB, sa0 + ((kt + 1) % SA) * OPER_BYTES,
+                                                     sb0 + ((kt + 1) % SB) * OPER_BYTES, fa, fb, acc, wm, wn, lane,
+                                                     la, lb, cA, lka, cB, lkb, ka_lim, kb_lim);
+    }
+    wait_vmcnt<0>();  // the trailing zero loads land before the epilogue reuses LDS
+    lds_barrier();
+    return;
+  }
   // stages past the end read as zero
   if (DEEP == 0) {
 #pragma unroll
@@ -704,7 +853,7 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
     DLoad la, lb;
     la.init(a.W, uint64_t(a.V) * a.D * 2, a.D, v0, a.V);
     lb.init(a.Hc, uint64_t(a.rows) * a.D * 2, a.D, p0, a.rows);
-    gemm_core<false, false, KD_DEEP_LOGITS>(la, lb, 0, a.D, a.D, a.D, acc, smem);
+    gemm_core<false, false, KD_DEEP_LOGITS, KD_EB_LOGITS>(la, lb, 0, a.D, a.D, a.D, acc, smem);
   }
 
   float* S = reinterpret_cast<float*>(smem);
@@ -1116,7 +1265,7 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
     MLoad lb;
     la.init(a.G, uint64_t(a.rows) * a.Vp * 2, a.Vp, tm * kTile, a.rows);
     lb.init(a.W, uint64_t(a.V) * a.D * 2, a.D, tn * kTile, a.D);
-    gemm_core<false, true, KD_DEEP_DH>(la, lb, k_begin, k_end, int(a.Vp), a.V, acc, smem);
+    gemm_core<false, true, KD_DEEP_DH, KD_EB_DH>(la, lb, k_begin, k_end, int(a.Vp), a.V, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -1174,7 +1323,7 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
     MLoad la, lb;
     la.init(a.G, uint64_t(a.rows) * a.Vp * 2, a.Vp, tm * kTile, int(a.Vp));
     lb.init(a.H, uint64_t(a.rows) * a.D * 2, a.D, tn * kTile, a.D);
-    gemm_core<true, true, KD_DEEP_DW>(la, lb, 0, a.rows, a.rows, a.rows, acc, smem);
+    gemm_core<true, true, KD_DEEP_DW, KD_EB_DW>(la, lb, 0, a.rows, a.rows, a.rows, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
