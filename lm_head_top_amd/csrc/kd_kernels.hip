@@ -70,6 +70,15 @@
 #ifndef KD_EB_DW
 #define KD_EB_DW 1
 #endif
+// dW tile order: 0 = D tile fastest; b > 0 = bands of b vocab tiles, vocab
+// tile fastest within a band
+#ifndef KD_DW_BAND
+#define KD_DW_BAND 4
+#endif
+// dH tile order: bands of this many row tiles, row tile fastest
+#ifndef KD_DH_BAND
+#define KD_DH_BAND 4
+#endif
 // Operand given a third LDS slot, so its loads run two stages ahead:
 // 0 none, 1 A, 2 B (per GEMM kernel; two-slot rings only)
 #ifndef KD_DEEP_LOGITS
@@ -1251,9 +1260,10 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
   const int sp = tile / tiles, rem = tile - sp * tiles;
   // bands of up to 4 row tiles, row tile fastest: the 32 tiles an XCD runs at
   // once cover 4 row tiles x 8 column tiles, whose operand strips its L2 shares
-  const int band = rem / (4 * tiles_n), bh = min(4, tiles_m - 4 * band);
-  const int bi = rem - band * 4 * tiles_n;
-  const int tm = 4 * band + bi % bh, tn = bi / bh;
+  constexpr int HB = KD_DH_BAND;
+  const int band = rem / (HB * tiles_n), bh = min(HB, tiles_m - HB * band);
+  const int bi = rem - band * HB * tiles_n;
+  const int tm = HB * band + bi % bh, tn = bi / bh;
   const int k_begin = sp * a.ktiles_per_split * BK;
   int k_end = k_begin + a.ktiles_per_split * BK;
   if (k_end > a.Vp) k_end = int(a.Vp);
@@ -1315,7 +1325,17 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
   const int tiles_m = int((a.V + kTile - 1) / kTile);
   const int tiles_n = (a.D + kTile - 1) / kTile;
   const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  int tm, tn;
+  if (KD_DW_BAND > 0) {
+    constexpr int B = KD_DW_BAND > 0 ? KD_DW_BAND : 1;
+    const int band = tile / (B * tiles_n), bh = min(B, tiles_m - B * band);
+    const int bi = tile - band * B * tiles_n;
+    tm = B * band + bi % bh;
+    tn = bi / bh;
+  } else {
+    tm = tile / tiles_n;
+    tn = tile - tm * tiles_n;
+  }
   f32x16 acc[MI][NJ];
   {
     // A = G^T and B = H^T of the chunk group, both read k-major from G
