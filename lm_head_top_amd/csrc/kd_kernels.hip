@@ -40,35 +40,38 @@
 
 #include "kd_kernels.h"
 
+// Build knobs (defaults are the measured best on MI355X)
 #ifndef KD_BK
-#define KD_BK 64
-#endif
-#ifndef KD_STAGES
-#define KD_STAGES 2
+#define KD_BK 64  // K depth of one pipeline stage
 #endif
 #ifndef KD_WAVES
-#define KD_WAVES 8
-#endif
-#ifndef KD_LPS
-#define KD_LPS (KD_WAVES == 8 ? 4 : 4)
-#endif
-#ifndef KD_VSPREAD
-#define KD_VSPREAD 0
+#define KD_WAVES 8  // waves per GEMM workgroup: 8 (two per SIMD) or 4
 #endif
 #ifndef KD_LOAD_AUX
-#define KD_LOAD_AUX 0
+#define KD_LOAD_AUX 0  // cache-policy bits of the direct LDS loads
 #endif
-// 1: each stage's barrier sits in its last MFMA step, after that step's
-// fragments are in registers, so the next stage's first fragment reads and
-// the ring refills overlap the step's MFMAs (per GEMM kernel)
-#ifndef KD_EB_LOGITS
-#define KD_EB_LOGITS 0
+// Operand given a third LDS slot, so its loads run two stages ahead:
+// 0 none, 1 A, 2 B (per GEMM kernel)
+#ifndef KD_DEEP_LOGITS
+#define KD_DEEP_LOGITS 1
 #endif
-#ifndef KD_EB_DH
-#define KD_EB_DH 1
+#ifndef KD_DEEP_DH
+#define KD_DEEP_DH 0
 #endif
-#ifndef KD_EB_DW
-#define KD_EB_DW 1
+#ifndef KD_DEEP_DW
+#define KD_DEEP_DW 0
+#endif
+// Ring loads of a stage: 0 = both operands' go out after the stage barrier
+// in the last MFMA step; 1 = only the operand that must land first does, the
+// other's go out in the next stage's first step (per GEMM kernel)
+#ifndef KD_SPLIT_LOGITS
+#define KD_SPLIT_LOGITS 1
+#endif
+#ifndef KD_SPLIT_DH
+#define KD_SPLIT_DH 0
+#endif
+#ifndef KD_SPLIT_DW
+#define KD_SPLIT_DW 0
 #endif
 // dW tile order: 0 = D tile fastest; b > 0 = bands of b vocab tiles, vocab
 // tile fastest within a band
@@ -78,17 +81,6 @@
 // dH tile order: bands of this many row tiles, row tile fastest
 #ifndef KD_DH_BAND
 #define KD_DH_BAND 4
-#endif
-// Operand given a third LDS slot, so its loads run two stages ahead:
-// 0 none, 1 A, 2 B (per GEMM kernel; two-slot rings only)
-#ifndef KD_DEEP_LOGITS
-#define KD_DEEP_LOGITS 1
-#endif
-#ifndef KD_DEEP_DH
-#define KD_DEEP_DH 0
-#endif
-#ifndef KD_DEEP_DW
-#define KD_DEEP_DW 0
 #endif
 
 namespace kd {
@@ -104,7 +96,7 @@ constexpr int WT_N = kTile / WAVES_N;            // wave tile columns (64 or 128
 constexpr int MI = WT_M / 32;                    // 32-row MFMA blocks per wave
 constexpr int NJ = WT_N / 32;                    // 32-column MFMA blocks per wave
 constexpr int BK = KD_BK;                        // K columns per pipeline stage
-constexpr int STAGES = KD_STAGES;                // LDS ring depth
+constexpr int STAGES = 2;                        // LDS slots per operand (a deep operand has 3)
 constexpr int CH = BK / 8;                       // 16-byte chunks per LDS row
 constexpr int ROWB = BK * 2;                     // bytes per LDS row
 constexpr int RPI = 64 / CH;                     // rows covered by one 1 KiB direct load
@@ -115,7 +107,6 @@ constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
 // LDS of the main loop when one operand has a third slot
 constexpr int ring_bytes(int deep) { return deep ? MAIN_BYTES + OPER_BYTES : MAIN_BYTES; }
 constexpr int NS = BK / 16;                      // 16-deep MFMA steps per stage
-constexpr int LPS = KD_LPS;                      // ring loads issued per MFMA step (front-loaded)
 constexpr int SLD = kTile + 4;                   // fp32 row stride of the epilogue staging tile
 constexpr int STAGE_FLOATS = 128 * SLD;          // half a tile: 128 positions x 256 vocab
 constexpr int EPI_BYTES = (STAGE_FLOATS + 10 * kTile) * 4;
@@ -126,10 +117,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 static_assert(BK == 32 || BK == 64, "BK");
 static_assert(WAVES == 4 || WAVES == 8, "WAVES");
-static_assert(LPS > 0 && LPS <= MI * NJ && (2 * NI) % LPS == 0 && 2 * NI <= LPS * NS, "LPS");
-static_assert(STAGES >= 2, "STAGES");
 static_assert(SMEM_BYTES <= 160 * 1024 && ring_bytes(1) <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-static_assert(STAGES == 2 || (KD_DEEP_LOGITS == 0 && KD_DEEP_DH == 0 && KD_DEEP_DW == 0), "deep slot");
 
 // GEMM kernels: one workgroup per compute unit; with 4 waves each wave may use
 // the whole register file of its SIMD (accumulators in AGPRs).
@@ -328,85 +316,11 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* tile, int col0, int s, int
 
 // --------------------------------------------------------------- MFMA core ---
 
-// One BK-deep stage of the wave's WT_M x WT_N tile.  MFMA 32x32x16 operands:
-// lane l supplies row l % 32 and the 8 consecutive k of half l / 32; an
-// operand tile is row-major with k contiguous (AMN / BMN false, one
-// ds_read_b128 per fragment) or k-major (true, two transposing reads).
-// Fragments of the next 16-deep step load while the current step multiplies,
-// and the next stage's ring loads (2 * NI per wave) go out LPS per step, each
-// between two MFMAs.
-template <bool AMN, bool BMN, bool B_FIRST, class LA, class LB>
-__device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const char* __restrict__ sB,
-                                          f32x16 (&acc)[MI][NJ], int wm, int wn, int lane,
-                                          const LA& la, const LB& lb, char* nA, int nka, char* nB,
-                                          int nkb, int ka_lim, int kb_lim) {
-  constexpr int NR = (AMN ? 2 : 1) * MI + (BMN ? 2 : 1) * NJ;  // fragment reads per step
-  constexpr int NQ = MI * NJ;                                  // MFMAs per step
-  const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31);   // K-contiguous tile rows are r31 mod 32
-  const int mo = mn_lane_off(lane);
-  const char* pa = sA + (wm * WT_M + r31) * ROWB;
-  const char* pb = sB + (wn * WT_N + r31) * ROWB;
-  auto read_a = [&](int i, int st) -> bf16x8 {
-    if constexpr (AMN) return frag_mn(sA, wm * WT_M + i * 32, st, lane, mo);
-    else return *reinterpret_cast<const bf16x8*>(pa + i * 32 * ROWB + (((2 * st + hi) ^ sw) * 16));
-  };
-  auto read_b = [&](int j, int st) -> bf16x8 {
-    if constexpr (BMN) return frag_mn(sB, wn * WT_N + j * 32, st, lane, mo);
-    else return *reinterpret_cast<const bf16x8*>(pb + j * 32 * ROWB + (((2 * st + hi) ^ sw) * 16));
-  };
-  bf16x8 fa[2][MI], fb[2][NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) fa[0][i] = read_a(i, 0);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) fb[0][j] = read_b(j, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // the first step's fragment reads
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < NS) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) fa[cur ^ 1][i] = read_a(i, s + 1);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) fb[cur ^ 1][j] = read_b(j, s + 1);
-    }
-    constexpr int NL = 2 * NI;
-    const int l0 = s * LPS;
-#pragma unroll
-    for (int q = 0; q < LPS; ++q) {
-      const int l = l0 + q;
-      // the operand loaded first is the one that must land by the next stage
-      if (l < NI) {
-        if (B_FIRST) lb.issue_one(l, nB, nkb, kb_lim);
-        else la.issue_one(l, nA, nka, ka_lim);
-      } else if (l < NL) {
-        if (B_FIRST) la.issue_one(l - NI, nA, nka, ka_lim);
-        else lb.issue_one(l - NI, nB, nkb, kb_lim);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-    // NQ MFMAs; between them go the next step's fragment reads (spread
-    // evenly) and this step's ring loads (one after each of the first MFMAs,
-    // or spread)
-    const int nl = l0 < NL ? (NL - l0 < LPS ? NL - l0 : LPS) : 0;
-    const int nr = s + 1 < NS ? NR : 0;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      const int rq = (nr * (q + 1)) / NQ - (nr * q) / NQ;
-#pragma unroll
-      for (int u = 0; u < rq; ++u) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (KD_VSPREAD ? (nl > 0 && q % (NQ / LPS) == 0 && q / (NQ / LPS) < nl) : (q < nl))
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-  }
-}
-
-// acc[i][j] (wave (wm, wn) = (wave / WAVES_N, wave % WAVES_N)) register r holds C[m][n] with
-//   m = wm*WT_M + i*32 + 8*(r/4) + 4*(lane/32) + r%4,   n = wn*WT_N + j*32 + lane%32.
+// MFMA 32x32x16 operands: lane l supplies row l % 32 and the 8 consecutive k
+// of half l / 32; an operand tile is row-major with k contiguous (AMN / BMN
+// false, one ds_read_b128 per fragment) or k-major (true, two transposing
+// reads).
+//
 // One BK-deep stage with the barrier in its last step.  On entry fa[0] and
 // fb[0] hold the stage's first-step fragments; steps read the next step's
 // fragments while they multiply.  In the last step the wave waits for its own
@@ -415,13 +329,17 @@ __device__ __forceinline__ void mma_stage(const char* __restrict__ sA, const cha
 // stage's slots and the next stage has landed.  It then reads the next
 // stage's first-step fragments from nsA / nsB (into fa[0] / fb[0]) and
 // refills this stage's slots (ring loads to ldA / ldB, the operand that must
-// land first going out first) while the last step's MFMAs run.
-template <bool AMN, bool BMN, bool B_FIRST, int VMW, class LA, class LB>
+// land first going out first) while the last step's MFMAs run.  With SPLIT
+// only that operand goes out there; the other one's loads (to dd at dk) go
+// out in the first step of the stage, for the slot the previous barrier
+// freed.
+template <bool AMN, bool BMN, bool B_FIRST, int VMW, bool SPLIT, class LA, class LB>
 __device__ __forceinline__ void mma_stage_eb(const char* __restrict__ sA, const char* __restrict__ sB,
                                              const char* __restrict__ nsA, const char* __restrict__ nsB,
                                              bf16x8 (&fa)[2][MI], bf16x8 (&fb)[2][NJ], f32x16 (&acc)[MI][NJ],
                                              int wm, int wn, int lane, const LA& la, const LB& lb, char* ldA,
-                                             int lka, char* ldB, int lkb, int ka_lim, int kb_lim) {
+                                             int lka, char* ldB, int lkb, char* dd, int dk, int ka_lim,
+                                             int kb_lim) {
   constexpr int NR = (AMN ? 2 : 1) * MI + (BMN ? 2 : 1) * NJ;  // fragment reads per step
   constexpr int NQ = MI * NJ;                                  // MFMAs per step
   constexpr int NL = 2 * NI;                                   // ring loads per stage
@@ -445,17 +363,29 @@ __device__ __forceinline__ void mma_stage_eb(const char* __restrict__ sA, const 
     for (int i = 0; i < MI; ++i) fa[cur ^ 1][i] = read_a(sA, i, s + 1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[cur ^ 1][j] = read_b(sB, j, s + 1);
+    // deferred ring loads of the operand that lands second (SPLIT)
+    if (SPLIT && s == 0) {
+#pragma unroll
+      for (int l = 0; l < NI; ++l) {
+        if (B_FIRST) la.issue_one(l, dd, dk, ka_lim);
+        else lb.issue_one(l, dd, dk, kb_lim);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+    const int nl = SPLIT && s == 0 ? NI : 0;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       const int rq = (NR * (q + 1)) / NQ - (NR * q) / NQ;
 #pragma unroll
       for (int u = 0; u < rq; ++u) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      const int lq = (nl * (q + 1)) / NQ - (nl * q) / NQ;
+#pragma unroll
+      for (int u = 0; u < lq; ++u) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   }
   constexpr int cur = (NS - 1) & 1;
@@ -465,8 +395,9 @@ __device__ __forceinline__ void mma_stage_eb(const char* __restrict__ sA, const 
   for (int i = 0; i < MI; ++i) fa[cur ^ 1][i] = read_a(nsA, i, 0);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) fb[cur ^ 1][j] = read_b(nsB, j, 0);
+  constexpr int NLL = SPLIT ? NI : NL;  // ring loads in this step
 #pragma unroll
-  for (int l = 0; l < NL; ++l) {
+  for (int l = 0; l < NLL; ++l) {
     if (l < NI) {
       if (B_FIRST) lb.issue_one(l, ldB, lkb, kb_lim);
       else la.issue_one(l, ldA, lka, ka_lim);
@@ -486,24 +417,31 @@ __device__ __forceinline__ void mma_stage_eb(const char* __restrict__ sA, const 
     const int rq = (NR * (q + 1)) / NQ - (NR * q) / NQ;
 #pragma unroll
     for (int u = 0; u < rq; ++u) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    const int lq = (NL * (q + 1)) / NQ - (NL * q) / NQ;
+    const int lq = (NLL * (q + 1)) / NQ - (NLL * q) / NQ;
 #pragma unroll
     for (int u = 0; u < lq; ++u) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 }
 
-// DEEP = 1 (2): operand A (B) has three LDS slots and its loads run two
-// stages ahead; the other operand's loads go out first in each stage, so one
-// vmcnt wait that leaves only the deep operand's newest loads in flight
-// covers both operands of the current stage.  LDS holds the A slots, then the
-// B slots, OPER_BYTES each (ring_bytes(DEEP) in all).
-template <bool AMN = false, bool BMN = false, int DEEP = 0, bool EB = false, class LA, class LB>
+// Multiplies the 256 x 256 tile over k in [k_begin, k_end) into acc.  The
+// operands stream into an LDS ring, OPER_BYTES per slot: the A slots, then
+// the B slots (ring_bytes(DEEP) in all).  Each operand has two slots, or
+// three for the DEEP one (1: A, 2: B), whose loads then run two stages
+// ahead.  The loads of an operand's stage s go to slot s % slots; stages past
+// the end load zeros that nothing reads.
+//
+// Stage kt's barrier sits in its last MFMA step (mma_stage_eb).  After it,
+// stage kt's slots take the operand stages kt + slots: the operand that must
+// land first (B when A is deep, else A) goes out at once; the other one goes
+// out there too, or with SPLIT in the next stage's first step.  The wave's
+// wait before each barrier leaves in flight only the loads issued after the
+// next stage's, so one wait and the barrier cover both operands of it.
+template <bool AMN, bool BMN, int DEEP, bool SPLIT, class LA, class LB>
 __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int k_begin, int k_end,
                                           int ka_lim, int kb_lim, f32x16 (&acc)[MI][NJ], char* smem) {
-  static_assert(DEEP >= 0 && DEEP <= 2 && (DEEP == 0 || STAGES == 2), "DEEP");
+  static_assert(DEEP >= 0 && DEEP <= 2, "DEEP");
   constexpr int SA = STAGES + (DEEP == 1 ? 1 : 0);  // A slots
   constexpr int SB = STAGES + (DEEP == 2 ? 1 : 0);  // B slots
-  constexpr int AHEAD_A = SA - 1, AHEAD_B = SB - 1;  // stages each operand loads ahead
   constexpr bool B_FIRST = DEEP == 1;
   char* const sa0 = smem;
   char* const sb0 = smem + SA * OPER_BYTES;
@@ -517,77 +455,47 @@ __device__ __forceinline__ void gemm_core(const LA& la, const LB& lb, int k_begi
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (k_end - k_begin + BK - 1) / BK;
   if (nk <= 0) return;
-  if (EB) {
-    // loads of stage s of an operand go to slot s % slots; stages past the
-    // end read as zero.  Prologue: A0 B0 A1 B1, then A2 (DEEP 1) or B2 (DEEP 2).
-    la.issue(sa0, k_begin, ka_lim);
-    lb.issue(sb0, k_begin, kb_lim);
-    la.issue(sa0 + OPER_BYTES, 1 < nk ? k_begin + BK : 0x3fffffff, ka_lim);
-    lb.issue(sb0 + OPER_BYTES, 1 < nk ? k_begin + BK : 0x3fffffff, kb_lim);
-    if (DEEP == 1) la.issue(sa0 + 2 * OPER_BYTES, 2 < nk ? k_begin + 2 * BK : 0x3fffffff, ka_lim);
-    if (DEEP == 2) lb.issue(sb0 + 2 * OPER_BYTES, 2 < nk ? k_begin + 2 * BK : 0x3fffffff, kb_lim);
-    wait_vmcnt<(DEEP ? 3 : 2) * NI>();  // stage 0 of both operands
-    lds_barrier();
-    bf16x8 fa[2][MI], fb[2][NJ];
-    {
-      const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31), mo = mn_lane_off(lane);
+  // Prologue: A0 B0 A1 B1, then A2 (DEEP 1) or B2 (DEEP 2).  With SPLIT the
+  // last of these (B1 when DEEP is 0) goes out in stage 0's first step
+  // instead, as the second operand's loads of every later stage do.
+  la.issue(sa0, k_begin, ka_lim);
+  lb.issue(sb0, k_begin, kb_lim);
+  la.issue(sa0 + OPER_BYTES, 1 < nk ? k_begin + BK : 0x3fffffff, ka_lim);
+  if (!SPLIT || DEEP) lb.issue(sb0 + OPER_BYTES, 1 < nk ? k_begin + BK : 0x3fffffff, kb_lim);
+  if (!SPLIT && DEEP == 1) la.issue(sa0 + 2 * OPER_BYTES, 2 < nk ? k_begin + 2 * BK : 0x3fffffff, ka_lim);
+  if (!SPLIT && DEEP == 2) lb.issue(sb0 + 2 * OPER_BYTES, 2 < nk ? k_begin + 2 * BK : 0x3fffffff, kb_lim);
+  // stage 0 of both operands has landed once only the loads issued after it remain
+  wait_vmcnt<(DEEP ? 3 : 2) * NI - (SPLIT ? NI : 0)>();
+  lds_barrier();
+  bf16x8 fa[2][MI], fb[2][NJ];
+  {
+    const int r31 = lane & 31, hi = lane >> 5, sw = swz(r31), mo = mn_lane_off(lane);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        if constexpr (AMN) fa[0][i] = frag_mn(sa0, wm * WT_M + i * 32, 0, lane, mo);
-        else fa[0][i] = *reinterpret_cast<const bf16x8*>(sa0 + (wm * WT_M + i * 32 + r31) * ROWB + ((hi ^ sw) * 16));
-      }
+    for (int i = 0; i < MI; ++i) {
+      if constexpr (AMN) fa[0][i] = frag_mn(sa0, wm * WT_M + i * 32, 0, lane, mo);
+      else fa[0][i] = *reinterpret_cast<const bf16x8*>(sa0 + (wm * WT_M + i * 32 + r31) * ROWB + ((hi ^ sw) * 16));
+    }
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if constexpr (BMN) fb[0][j] = frag_mn(sb0, wn * WT_N + j * 32, 0, lane, mo);
-        else fb[0][j] = *reinterpret_cast<const bf16x8*>(sb0 + (wn * WT_N + j * 32 + r31) * ROWB + ((hi ^ sw) * 16));
-      }
+    for (int j = 0; j < NJ; ++j) {
+      if constexpr (BMN) fb[0][j] = frag_mn(sb0, wn * WT_N + j * 32, 0, lane, mo);
+      else fb[0][j] = *reinterpret_cast<const bf16x8*>(sb0 + (wn * WT_N + j * 32 + r31) * ROWB + ((hi ^ sw) * 16));
     }
-    for (int kt = 0; kt < nk; ++kt) {
-      // after this stage's barrier its slots take stage kt + slots; the
-      // next stage's operands come from slot (kt + 1) % slots
-      const int na = kt + SA, nb = kt + SB;
-      const int lka = na < nk ? k_begin + na * BK : 0x3fffffff;
-      const int lkb = nb < nk ? k_begin + nb * BK : 0x3fffffff;
-      char* const cA = sa0 + (kt % SA) * OPER_BYTES;
-      char* const cB = sb0 + (kt % SB) * OPER_BYTES;
-      mma_stage_eb<AMN, BMN, B_FIRST, DEEP ? NI : 0>(cA, cB, sa0 + ((kt + 1) % SA) * OPER_BYTES,
-                                                     sb0 + ((kt + 1) % SB) * OPER_BYTES, fa, fb, acc, wm, wn, lane,
-                                                     la, lb, cA, lka, cB, lkb, ka_lim, kb_lim);
-    }
-    wait_vmcnt<0>();  // the trailing zero loads land before the epilogue reuses LDS
-    lds_barrier();
-    return;
-  }
-  // stages past the end read as zero
-  if (DEEP == 0) {
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-      la.issue(sa0 + s * OPER_BYTES, k_begin + s * BK, ka_lim);
-      lb.issue(sb0 + s * OPER_BYTES, k_begin + s * BK, kb_lim);
-    }
-  } else if (DEEP == 1) {
-    la.issue(sa0, k_begin, ka_lim);
-    lb.issue(sb0, k_begin, kb_lim);
-    la.issue(sa0 + OPER_BYTES, k_begin + BK, ka_lim);
-  } else {
-    lb.issue(sb0, k_begin, kb_lim);
-    la.issue(sa0, k_begin, ka_lim);
-    lb.issue(sb0 + OPER_BYTES, k_begin + BK, kb_lim);
   }
   for (int kt = 0; kt < nk; ++kt) {
-    // every iteration issues one stage of each operand; once only the newer
-    // loads allowed in flight remain, stage kt of both operands has landed
-    if (DEEP == 0) wait_vmcnt<(STAGES - 2) * 2 * NI>();
-    else wait_vmcnt<NI>();
-    lds_barrier();
-    // the next loads refill the slots every wave finished reading last
-    // iteration; near the end they load zeros that nothing reads
-    const int na = kt + AHEAD_A, nb = kt + AHEAD_B;
-    const int nka = na < nk ? k_begin + na * BK : 0x3fffffff;
-    const int nkb = nb < nk ? k_begin + nb * BK : 0x3fffffff;
-    mma_stage<AMN, BMN, B_FIRST>(sa0 + (kt % SA) * OPER_BYTES, sb0 + (kt % SB) * OPER_BYTES, acc, wm, wn, lane,
-                                 la, lb, sa0 + (na % SA) * OPER_BYTES, nka, sb0 + (nb % SB) * OPER_BYTES, nkb,
-                                 ka_lim, kb_lim);
+    const int na = kt + SA, nb = kt + SB;
+    const int lka = na < nk ? k_begin + na * BK : 0x3fffffff;
+    const int lkb = nb < nk ? k_begin + nb * BK : 0x3fffffff;
+    char* const cA = sa0 + (kt % SA) * OPER_BYTES;
+    char* const cB = sb0 + (kt % SB) * OPER_BYTES;
+    // SPLIT: the operand loaded second takes its stage kt + slots - 1 in this
+    // stage's first step, into the slot freed by the previous barrier
+    constexpr int SX = B_FIRST ? SA : SB;
+    const int nd = kt + SX - 1;
+    char* const dd = (B_FIRST ? sa0 : sb0) + (nd % SX) * OPER_BYTES;
+    const int dk = nd < nk ? k_begin + nd * BK : 0x3fffffff;
+    mma_stage_eb<AMN, BMN, B_FIRST, DEEP ? NI : 0, SPLIT>(cA, cB, sa0 + ((kt + 1) % SA) * OPER_BYTES,
+                                                          sb0 + ((kt + 1) % SB) * OPER_BYTES, fa, fb, acc, wm, wn,
+                                                          lane, la, lb, cA, lka, cB, lkb, dd, dk, ka_lim, kb_lim);
   }
   wait_vmcnt<0>();  // the trailing zero loads land before the epilogue reuses LDS
   lds_barrier();
@@ -862,7 +770,7 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
     DLoad la, lb;
     la.init(a.W, uint64_t(a.V) * a.D * 2, a.D, v0, a.V);
     lb.init(a.Hc, uint64_t(a.rows) * a.D * 2, a.D, p0, a.rows);
-    gemm_core<false, false, KD_DEEP_LOGITS, KD_EB_LOGITS>(la, lb, 0, a.D, a.D, a.D, acc, smem);
+    gemm_core<false, false, KD_DEEP_LOGITS, KD_SPLIT_LOGITS != 0>(la, lb, 0, a.D, a.D, a.D, acc, smem);
   }
 
   float* S = reinterpret_cast<float*>(smem);
@@ -1275,7 +1183,7 @@ KD_GEMM_KERNEL void dh_kernel(DhArgs a) {
     MLoad lb;
     la.init(a.G, uint64_t(a.rows) * a.Vp * 2, a.Vp, tm * kTile, a.rows);
     lb.init(a.W, uint64_t(a.V) * a.D * 2, a.D, tn * kTile, a.D);
-    gemm_core<false, true, KD_DEEP_DH, KD_EB_DH>(la, lb, k_begin, k_end, int(a.Vp), a.V, acc, smem);
+    gemm_core<false, true, KD_DEEP_DH, KD_SPLIT_DH != 0>(la, lb, k_begin, k_end, int(a.Vp), a.V, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -1343,7 +1251,7 @@ KD_GEMM_KERNEL void dw_kernel(DwArgs a) {
     MLoad la, lb;
     la.init(a.G, uint64_t(a.rows) * a.Vp * 2, a.Vp, tm * kTile, int(a.Vp));
     lb.init(a.H, uint64_t(a.rows) * a.D * 2, a.D, tn * kTile, a.D);
-    gemm_core<true, true, KD_DEEP_DW, KD_EB_DW>(la, lb, 0, a.rows, a.rows, a.rows, acc, smem);
+    gemm_core<true, true, KD_DEEP_DW, KD_SPLIT_DW != 0>(la, lb, 0, a.rows, a.rows, a.rows, acc, smem);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
