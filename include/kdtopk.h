@@ -74,13 +74,13 @@ typedef enum kd_status {
  * Bytes of device workspace that kd_topk_kl_forward and kd_topk_kl_backward
  * need for this problem (one size serves both).  Depends only on the
  * arguments, never on the device.  Returns 0 for arguments that the entry
- * points would reject.  The workspace holds one chunk's teacher
- * probabilities and id buckets, the forward's per-vocab-tile softmax
- * partials and, for the backward, the bf16 gradient rows G of one group of
- * consecutive chunks (the fewest whole chunks that hold 8192 positions, at
- * most 8 chunks and at most N positions) with fp32 split partials for dH
- * when a block of rows is too small to fill the device.  The size is
- * O(R * V + chunk * K) bytes plus 4 N bytes, where R is the
+ * points would reject.  The workspace holds the teacher probabilities and
+ * id buckets of one group of consecutive chunks (the fewest whole chunks
+ * that hold 8192 positions, at most 8 chunks and at most N positions), the
+ * forward's per-vocab-tile softmax partials of one chunk and, for the
+ * backward, the bf16 gradient rows G of one group with fp32 split partials
+ * for dH when a block of rows is too small to fill the device.  The size is
+ * O(R * V + R * K) bytes plus 4 N bytes, where R is the
  * group's rows (at most max(chunk, 8192) rounded to whole chunks): bounded
  * in N, never O(N * V).
  */

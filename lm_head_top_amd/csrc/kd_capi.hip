@@ -105,6 +105,35 @@ struct LossExt {
   float alpha = 1.f, beta = 0.f, scale = 1.f;
 };
 
+// Teacher probabilities and id buckets for the group of chunks that starts
+// at row0: up to p.dw_group chunks, one launch each over all of them.  Chunk
+// j's rows sit at j * chunk in pw / hw and its buckets at j * boff_stride /
+// j * ent_stride.
+kd_status prepare_group(const kd::Plan& p, const int32_t* topk_idx, const float* topk_logit,
+                        const int32_t* labels, int64_t N, int64_t V, int32_t K, int KE, float invT,
+                        int64_t row0, float* pw, float* hw, int32_t* boff, uint32_t* ent, hipStream_t s) {
+  const int64_t span = int64_t(p.dw_group) * p.chunk;
+  const int grows = int(N - row0 < span ? N - row0 : span);
+  const int nch = int((grows + p.chunk - 1) / p.chunk);
+  kd::TeacherArgs ta{topk_logit + row0 * K, grows, K, invT, pw, hw};
+  KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
+  kd::BucketArgs ba{};
+  ba.idx = topk_idx + row0 * K;
+  ba.rows = grows;
+  ba.K = K;
+  ba.V = int(V);
+  ba.nvt = int(p.nvt);
+  ba.chunk = int(p.chunk);
+  ba.KE = KE;
+  ba.labels = labels != nullptr ? labels + row0 : nullptr;
+  ba.boff = boff;
+  ba.ent = ent;
+  ba.boff_stride = p.boff_stride;
+  ba.ent_stride = p.ent_stride;
+  KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, int(p.npt), nch, s));
+  return KD_OK;
+}
+
 // The forward's chunk loop.  With zkeep / gall set (kept-gradient mode) each
 // chunk's fp32 logits are kept and turned into its G rows of gall.
 kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
@@ -122,23 +151,21 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
   const float invT = 1.f / T;
   const float g_scale = float(1.0 / (double(N) * double(T)));
 
+  const int KE = K + (ext.labels != nullptr ? 1 : 0);
+  int gj = 0;  // chunk within its group
   for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
     const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
     const int npt = (rows + kd::kTile - 1) / kd::kTile;
-    kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
-    KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
-    const int KE = K + (ext.labels != nullptr ? 1 : 0);
-    kd::BucketArgs ba{};
-    ba.idx = topk_idx + row0 * K;
-    ba.rows = rows;
-    ba.K = K;
-    ba.V = int(V);
-    ba.nvt = int(p.nvt);
-    ba.KE = KE;
-    ba.labels = ext.labels != nullptr ? ext.labels + row0 : nullptr;
-    ba.boff = boff;
-    ba.ent = ent;
-    KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, npt, s));
+    if (gj == 0) {
+      const kd_status st =
+          prepare_group(p, topk_idx, topk_logit, ext.labels, N, V, K, KE, invT, row0, pw, hw, boff, ent, s);
+      if (st != KD_OK) return st;
+    }
+    float* const pc = pw + int64_t(gj) * p.chunk * K;
+    float* const hc = hw + int64_t(gj) * p.chunk;
+    int32_t* const boffc = boff + gj * p.boff_stride;
+    uint32_t* const entc = ent + gj * p.ent_stride;
+    gj = gj + 1 == p.dw_group ? 0 : gj + 1;
     kd::LogitsArgs la{};
     la.KE = KE;
     la.W = W;
@@ -152,8 +179,8 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
     la.c_pad = p.c_pad;
     la.Vp = p.Vp;
     la.invT = invT;
-    la.boff = boff;
-    la.ent = ent;
+    la.boff = boffc;
+    la.ent = entc;
     la.zkeep = zkeep;
     la.pm = pm;
     la.ps = ps;
@@ -163,8 +190,8 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
     ca.pm = pm;
     ca.ps = ps;
     ca.zsel = zsel;
-    ca.p = pw;
-    ca.h = hw;
+    ca.p = pc;
+    ca.h = hc;
     ca.rows = rows;
     ca.K = K;
     ca.nvt = int(p.nvt);
@@ -180,7 +207,7 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
     KD_LAUNCH(KD_KERNEL_COMBINE, s, kd::launch_combine(ca, s));
     if (zkeep != nullptr)
       KD_LAUNCH(KD_KERNEL_KEEP_GRAD, s,
-                kd::launch_keep_grad(zkeep, lse + row0, topk_idx + row0 * K, pw, rows, K, int(V), p.Vp,
+                kd::launch_keep_grad(zkeep, lse + row0, topk_idx + row0 * K, pc, rows, K, int(V), p.Vp,
                                      g_scale, gall + row0 * p.Vp, s));
   }
   KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, ext.row_w, N, loss, nullptr, s));
@@ -226,22 +253,14 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
     uint16_t* Gc = G + (row0 - group_row0) * p.Vp;
     kd::LogitsArgs la{};
     if (tlog == nullptr) {
-      kd::TeacherArgs ta{topk_logit + row0 * K, rows, K, invT, pw, hw};
-      KD_LAUNCH(KD_KERNEL_TEACHER, s, kd::launch_teacher(ta, s));
-      kd::BucketArgs ba{};
-      ba.idx = topk_idx + row0 * K;
-      ba.rows = rows;
-      ba.K = K;
-      ba.V = int(V);
-      ba.nvt = int(p.nvt);
-      ba.KE = KE;
-      ba.labels = ext.labels != nullptr ? ext.labels + row0 : nullptr;
-      ba.boff = boff;
-      ba.ent = ent;
-      KD_LAUNCH(KD_KERNEL_BUCKET, s, kd::launch_bucket(ba, npt, s));
-      la.boff = boff;
-      la.ent = ent;
-      la.p = pw;
+      if (gj == 0) {
+        const kd_status st =
+            prepare_group(p, topk_idx, topk_logit, ext.labels, N, V, K, KE, invT, row0, pw, hw, boff, ent, s);
+        if (st != KD_OK) return st;
+      }
+      la.boff = boff + gj * p.boff_stride;
+      la.ent = ent + gj * p.ent_stride;
+      la.p = pw + int64_t(gj) * p.chunk * K;
     } else {
       la.tlog = static_cast<const char*>(tlog) + row0 * V * esz;
       la.t_dtype = t_dtype;

@@ -19,13 +19,17 @@ struct TeacherArgs {
 };
 
 // Per-chunk cache entries bucketed by (position tile, vocab tile).
+// Buckets the cached ids of a run of consecutive chunks (chunk rows each, the
+// last one possibly shorter): block (pt, j) takes position tile pt of chunk j.
 struct BucketArgs {
-  const int32_t* idx;   // [rows, K], offset to the chunk's first row
-  int rows, K, V, nvt;
+  const int32_t* idx;   // [rows, K], offset to the first chunk's first row
+  int rows, K, V, nvt;  // rows: of all the chunks
+  int chunk;            // rows per chunk
   int KE;               // entries per row: K, or K + 1 with labels
-  const int32_t* labels;  // [rows] hard labels (offset to the chunk), or null
-  int32_t* boff;        // [npt, nvt + 1]
-  uint32_t* ent;        // [npt, kTile * K]
+  const int32_t* labels;  // [rows] hard labels (offset to the first chunk), or null
+  int32_t* boff;        // chunk j: [npt, nvt + 1] at j * boff_stride
+  uint32_t* ent;        // chunk j: [npt, kTile * KE] at j * ent_stride
+  int64_t boff_stride, ent_stride;
 };
 
 // The chunk's logits tile kernel: z^T = W H_c^T / T over one (vocab tile,
@@ -119,7 +123,7 @@ struct DwArgs {
 
 int gemm_bk();  // K depth of one GEMM pipeline stage
 hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s);
-hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s);
+hipError_t launch_bucket(const BucketArgs& a, int npt, int nchunks, hipStream_t s);
 hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

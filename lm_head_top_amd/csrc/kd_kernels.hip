@@ -594,15 +594,20 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   __shared__ int wsum[BT / 64];
   __shared__ uint32_t stage[kBucketStage];
   const int pt = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r0 = pt * kTile;
-  const int nr = min(kTile, a.rows - r0);
+  // this block's chunk: rows [crow0, crow0 + crows) of the run
+  const int crow0 = int(blockIdx.y) * a.chunk;
+  const int crows = min(a.chunk, a.rows - crow0);
+  const int r0 = pt * kTile;  // within the chunk
+  if (r0 >= crows) return;    // a tile past a short last chunk (the whole block)
+  const int nr = min(kTile, crows - r0);
   const int nvt = a.nvt;
+  const int32_t* labels = a.labels != nullptr ? a.labels + crow0 : nullptr;
   int bsh = 4;  // log2 of the counters per tile
   while (bsh > 0 && (nvt << bsh) > kBucketCnt) --bsh;
   const int nc = nvt << bsh;
   const int sub = lane & ((1 << bsh) - 1);
   const int nk = nr * a.K;  // cached entries of the tile
-  const int32_t* idx = a.idx + int64_t(r0) * a.K;
+  const int32_t* idx = a.idx + (int64_t(crow0) + r0) * a.K;
   const float invK = 1.f / float(a.K);
   int id[BU];
   auto load = [&](int e0) {
@@ -623,9 +628,9 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
     if (e0 >= nk) break;
     load(e0);
   }
-  if (a.labels != nullptr)
+  if (labels != nullptr)
     for (int rr = tid; rr < nr; rr += BT) {
-      const int y = a.labels[r0 + rr];
+      const int y = labels[r0 + rr];
       if (unsigned(y) < unsigned(a.V)) atomicAdd(&cnt[((y >> 8) << bsh) | sub], 1);
     }
   __syncthreads();
@@ -656,7 +661,7 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   __syncthreads();
   int run = (wave > 0 ? wsum[wave - 1] : 0) + x - loc;
   const int total = wsum[BT / 64 - 1];
-  int32_t* bo = a.boff + int64_t(pt) * (nvt + 1);
+  int32_t* bo = a.boff + int64_t(blockIdx.y) * a.boff_stride + int64_t(pt) * (nvt + 1);
   for (int q = 0; q < seg; ++q) {
     const int v = b0 + q;
     if (v < nc) {
@@ -668,7 +673,7 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
   }
   if (tid == BT - 1) bo[nvt] = total;
   __syncthreads();
-  uint32_t* ent = a.ent + int64_t(pt) * kTile * a.KE;
+  uint32_t* ent = a.ent + int64_t(blockIdx.y) * a.ent_stride + int64_t(pt) * kTile * a.KE;
   const bool in_lds = nr * a.KE <= kBucketStage;  // uniform
   uint32_t* dst = in_lds ? stage : ent;
   const bool multi = nk > BU * BT;  // else the ids are still in registers
@@ -687,9 +692,9 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
         dst[pos] = (uint32_t(rr) << 17) | (uint32_t(id[u] & (kTile - 1)) << 9) | uint32_t(k);
       }
   }
-  if (a.labels != nullptr)
+  if (labels != nullptr)
     for (int rr = tid; rr < nr; rr += BT) {
-      const int y = a.labels[r0 + rr];
+      const int y = labels[r0 + rr];
       if (unsigned(y) < unsigned(a.V)) {
         const int pos = atomicAdd(&cnt[((y >> 8) << bsh) | sub], 1);
         dst[pos] = (uint32_t(rr) << 17) | (uint32_t(y & (kTile - 1)) << 9) | uint32_t(a.K);
@@ -1357,8 +1362,8 @@ hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bucket(const BucketArgs& a, int npt, hipStream_t s) {
-  hipLaunchKernelGGL(bucket_kernel, dim3(npt), dim3(BT), 0, s, a);
+hipError_t launch_bucket(const BucketArgs& a, int npt, int nchunks, hipStream_t s) {
+  hipLaunchKernelGGL(bucket_kernel, dim3(npt, nchunks), dim3(BT), 0, s, a);
   return hipGetLastError();
 }
 

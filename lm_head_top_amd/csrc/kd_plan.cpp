@@ -81,12 +81,16 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
     off = align_up(off + bytes);
     return o;
   };
-  // teacher probabilities, per-row sum p log p, bucket offsets and entries
-  p.off_p = take(size_t(p.c_pad) * K * 4);
-  p.off_h = take(size_t(p.c_pad) * 4);
-  p.off_boff = take(size_t(p.npt) * size_t(p.nvt + 1) * 4);
+  // teacher probabilities, per-row sum p log p, bucket offsets and entries,
+  // for the dw_group chunks of a group
+  const size_t gch = size_t(p.dw_group);
+  p.boff_stride = p.npt * (p.nvt + 1);
+  p.ent_stride = p.npt * kTile * (int64_t(K) + 1);  // K cached ids and a label per row
+  p.off_p = take(gch * size_t(p.c_pad) * K * 4);
+  p.off_h = take(gch * size_t(p.c_pad) * 4);
+  p.off_boff = take(gch * size_t(p.boff_stride) * 4);
   p.off_scalar = take(256);  // 1 / sum of the row weights
-  p.off_ent = take(size_t(p.npt) * kTile * (K + 1) * 4);  // K cached ids and a label per row
+  p.off_ent = take(gch * size_t(p.ent_stride) * 4);
   const size_t shared_end = off;
   // forward-only region
   p.off_pm = take(size_t(p.nvt) * p.c_pad * 4);

@@ -28,6 +28,12 @@ struct Plan {
   int dw_group = 1;    // consecutive chunks whose G rows feed one dW GEMM (K = dw_group * chunk)
   int64_t grp_pad = 0; // rows of one dH GEMM over a group: min(group rows, kDhRows), rounded up to kTile
   int grp_split = 1;   // split-K factor of such a dH GEMM
+  // The teacher probabilities and the id buckets are formed for a group of
+  // dw_group chunks at once: chunk j of a group has its p and h rows at
+  // j * chunk and its bucket offsets and entries at j * boff_stride and
+  // j * ent_stride (elements).
+  int64_t boff_stride = 0;  // npt * (nvt + 1)
+  int64_t ent_stride = 0;   // npt * kTile * (K + 1)
   // workspace byte offsets
   size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0, off_scalar = 0;  // shared by fwd and bwd
   size_t off_pm = 0, off_ps = 0, off_zsel = 0, off_rowkl = 0;  // forward only

@@ -59,8 +59,12 @@ def test_workspace_size_scales_with_chunk_not_N(lib):
     b = f(32768, 4096, 131072, 100, 1024)
     # only the 4-byte-per-row KL buffer grows with N
     assert 0 <= b - a <= 4 * (32768 - 8192) + 512
+    # a group holds 8192 positions at chunk 1024 (8 chunks) and at 2048 (4)
     c = f(8192, 4096, 131072, 100, 2048)
-    assert c > a
+    assert c == a
+    # one chunk of 12288 positions is a group of its own: 4096 more G rows
+    d = f(32768, 4096, 131072, 100, 12288)
+    assert d > b + 131072 * 4096 * 2 - (64 << 20)
     # never O(N V): the dense fp32 grid at 32K x 131072 would be 16 GiB; the
     # workspace holds the G rows of one group of g chunks feeding the dH and
     # dW GEMMs (g = 8 at chunk 1024) plus per-chunk buffers: O(g chunk V)
