@@ -3,8 +3,11 @@
 
 One step = kd_topk_kl_forward + kd_topk_kl_backward over the whole batch of
 N positions (every chunk), with inputs already resident in device memory.
-Default workload: the toy LM head (N = 8192 positions, D = 4096,
-V = 131072, K = 100, chunk = 1024, T = 1), synthetic seeded inputs.
+Default workload: the very-long-context head (N = 262144 positions, D = 4096,
+V = 131072, K = 100, chunk = 4096, T = 1, fp32 dW accumulator), the largest
+of the workloads, synthetic seeded inputs.  The timed steps run without any
+per-kernel instrumentation; per-kernel averages come from a separate pass of
+--profile-steps steps after them.
 
 Prints one JSON line on stdout; everything else goes to stderr.
 """
@@ -31,9 +34,14 @@ GROUP_POSITIONS = 8192  # positions per dW GEMM of the library (whole chunks, at
 DH_ROWS = 4096          # rows per dH GEMM within such a group
 WORKLOAD_NAMES = {"tiny": "tiny", "toy": "toy_lm_head", "large_vocab": "large_vocab_head",
                   "long": "long_context", "very_long": "very_long_context"}
-# HBM traffic per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, with the
-# hash of the sources it was measured on (reported only while they are unchanged).
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+# HBM traffic per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, one file
+# per workload, with the hash of the sources it was measured on (reported only
+# while they are unchanged).
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
 KERNEL_SOURCES = ("lm_head_top_amd/csrc/kd_kernels.hip", "lm_head_top_amd/csrc/kd_kernels.h",
                   "lm_head_top_amd/csrc/kd_capi.hip", "lm_head_top_amd/csrc/kd_plan.cpp",
                   "lm_head_top_amd/csrc/kd_plan.h")
@@ -50,27 +58,62 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(inp, cfg, rows):
-    """The fp64 oracle, as it stands, on the first `rows` positions of the workload."""
-    import numpy as np
-    from oracle import kl_oracle as O
+def _host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _blas_info():
+    """(threads, library description) of numpy's BLAS, from threadpoolctl."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()
-                       if d.get("user_api") == "blas"] or [1])
+        blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
+        blas = []
+    if not blas:
+        return len(os.sched_getaffinity(0)), "unknown"
+    d = max(blas, key=lambda d: d.get("num_threads", 1))
+    lib = f"{d.get('internal_api', '?')} {d.get('version', '')} ({os.path.basename(d.get('filepath', ''))})"
+    return int(d.get("num_threads", 1)), lib.strip()
+
+
+def cpu_baseline(inp, cfg, rows, repeats=3):
+    """The fp64 oracle, as it stands, on the first `rows` positions of the
+    workload (row-blocked with the workload's chunk), median of `repeats`
+    runs.  Its cost per position does not depend on N (each block is an
+    independent dense problem against the same W), so the rate of the prefix
+    is the whole workload's rate, extrapolated linearly."""
+    import numpy as np
+    from oracle import kl_oracle as O
+    threads, blas = _blas_info()
     rows = min(rows, cfg.N)
     H = inp["H"][:rows]
     idx = inp["idx"][:rows]
     t = inp["t"][:rows]
-    t0 = time.perf_counter()
-    out = O.forward_backward_blocked(H, inp["W"], idx, t, cfg.T, block=min(cfg.chunk, rows))
-    dt = time.perf_counter() - t0
-    assert np.isfinite(out["loss"])
-    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} of {cfg.N} positions of the same workload (fp64 numpy, "
-                      f"row-blocked, block={min(cfg.chunk, rows)}); {dt:.1f} s wall"}
+    block = min(cfg.chunk, rows)
+    times = []
+    for _ in range(max(repeats, 1)):
+        t0 = time.perf_counter()
+        out = O.forward_backward_blocked(H, inp["W"], idx, t, cfg.T, block=block)
+        times.append(time.perf_counter() - t0)
+        assert np.isfinite(out["loss"])
+        del out
+    times.sort()
+    dt = times[len(times) // 2]
+    extrap = " extrapolated linearly in N" if rows < cfg.N else ""
+    return {"value": round(rows / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} of {cfg.N} positions of the same workload (fp64 numpy oracle, "
+                      f"row-blocked, block={block}), median of {len(times)} runs of "
+                      f"{', '.join(f'{x:.1f}' for x in times)} s;{extrap}",
+            "cpu_model": _host_cpu_model(), "blas": blas,
+            "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def code_text(src: str) -> str:
@@ -160,11 +203,12 @@ def write_traffic(fetch_dir, write_dir, copy_mib, command, config):
            "source_sha256": source_hash(), "sources": list(KERNEL_SOURCES),
            "calibration": {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale},
            "command": command, "config": config, "kernels": kernels}
-    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
-    with open(TRAFFIC_JSON, "w") as f:
+    out = traffic_path(config["workload"])
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
         f.write("\n")
-    log(f"wrote {TRAFFIC_JSON}: fetch scale {f_scale:.4f}, write scale {w_scale:.4f}")
+    log(f"wrote {out}: fetch scale {f_scale:.4f}, write scale {w_scale:.4f}")
     for cls, e in sorted(kernels.items()):
         log(f"  {cls:11s} {e['bytes_per_launch'] / 2**20:10.1f} MiB per launch")
 
@@ -199,10 +243,10 @@ def write_stats(stats_dir, out_path, command, bench_line=None):
 
 
 def measured_traffic(kernel: str, config: dict):
-    """Bytes per launch of `kernel` if profiles/traffic.json was taken on the
-    current sources and the same workload, else None."""
+    """Bytes per launch of `kernel` if the workload's traffic file was taken on
+    the current sources and the same workload, else None."""
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(traffic_path(config["workload"])) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
@@ -635,11 +679,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="toy", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--config", default=None, choices=sorted(WORKLOAD_NAMES),
+                    help="workload (default: very_long for the bench line, toy for the other modes)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=2048,
-                    help="positions of the CPU-oracle sample, about 10 s of fp64 work on 16 "
-                         "host threads at the toy head (0 skips it)")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="positions of the CPU-oracle sample (one 4096-position chunk of the "
+                         "default workload: about 13 s of fp64 work per run on 16 host threads; "
+                         "0 skips it)")
+    ap.add_argument("--cpu-repeats", type=int, default=3, help="runs of the CPU-oracle sample (median)")
+    ap.add_argument("--profile-steps", type=int, default=2,
+                    help="steps of the separate pass, after the timed steps, whose launches are "
+                         "bracketed by HIP events for the per-kernel averages")
+    ap.add_argument("--inputs-cache", default=None,
+                    help="directory for a .npz copy of the seeded inputs: loaded when present, "
+                         "written after drawing otherwise (saves the host draw in repeated runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain fp32 copy of this many MiB before warmup, as the known "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -674,6 +727,10 @@ def main():
     ap.add_argument("--blas-compare", action="store_true",
                     help="the four GEMM kernels beside hipBLASLt (torch.mm) on the same shapes of --config")
     args = ap.parse_args()
+    modes = (args.loss_ext, args.blas_compare, args.keep_compare, args.dense_teacher, args.memory_sweep,
+             args.dense_reference, args.topk_writer)
+    if args.config is None:
+        args.config = "toy" if any(modes) else "very_long"
     if args.gpus != 1 and not (args.stats_from or args.traffic_from):
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the loss runs on one "
               "device, and how it would shard over several is described, not implemented",
@@ -716,15 +773,15 @@ def main():
     import torch
 
     import lm_head_top_amd as kd
-    from synth import get_config, make_inputs
+    from synth import get_config
 
     kd.load_library()
     torch.cuda.set_device(0)
     cfg = get_config(args.config)
     log(f"workload {cfg}")
     t0 = time.perf_counter()
-    inp = make_inputs(cfg, args.seed)
-    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    inp = load_inputs(cfg, args.seed, args.inputs_cache)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     H = torch.from_numpy(inp["H"].view(np.int16)).view(torch.bfloat16).to(dev)
     W = torch.from_numpy(inp["W"].view(np.int16)).view(torch.bfloat16).to(dev)
@@ -748,16 +805,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.reset_peak_memory_stats()
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    kd.profile_enable(GEMM_KERNELS)
-    for k in GEMM_KERNELS:
-        kd.profile_read(k)  # drop anything recorded before the timed region
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    kd.profile_enable(None)  # the timed steps carry no per-kernel events
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    # per step: start, forward done, backward done
+    # per step: start, forward done, backward done (three events on the stream per step)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -771,7 +827,6 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    kd.profile_enable(None)
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
     fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
@@ -779,25 +834,34 @@ def main():
     step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
     med = lambda v: v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
     peak_gib = torch.cuda.max_memory_allocated() / 2**30
-    per_kernel = {}
-    for k in GEMM_KERNELS:
-        ms, n = kd.profile_read(k)
-        per_kernel[k] = {"total_ms": ms, "launches": n, "avg_ms": ms / max(n, 1)}
     flops_step = 8.0 * cfg.N * cfg.D * cfg.V
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = cfg.N / (ms_per_step * 1e-3)
     log(f"loss {loss.item():.6f}; {ms_per_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); "
         f"{tflops:.1f} TFLOP/s = {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak; "
         f"peak {peak_gib:.2f} GiB")
-    for k, v in per_kernel.items():
-        log(f"  {k:11s} {v['total_ms'] / args.steps:8.3f} ms/step over {v['launches']} launches, "
-            f"avg {v['avg_ms']:.3f} ms")
+
+    # Per-kernel averages: a separate pass whose GEMM launches are bracketed by
+    # HIP events the library records on the launch stream.
+    psteps = max(args.profile_steps, 1)
+    kd.profile_enable(GEMM_KERNELS)
+    for k in GEMM_KERNELS:
+        kd.profile_read(k)  # drop anything recorded before
+    for _ in range(psteps):
+        step()
+    torch.cuda.synchronize()
+    kd.profile_enable(None)
+    per_kernel = {}
+    for k in GEMM_KERNELS:
+        ms, n = kd.profile_read(k)
+        per_kernel[k] = {"total_ms": ms, "launches": n, "avg_ms": ms / max(n, 1)}
+        log(f"  {k:11s} {ms / psteps:8.3f} ms/step over {n} launches in {psteps} steps, "
+            f"avg {ms / max(n, 1):.3f} ms")
 
     dom = max(GEMM_KERNELS, key=lambda k: per_kernel[k]["total_ms"])
     dk = per_kernel[dom]
     # each GEMM kind does 2 N D V flops per step in total, spread over its launches
-    flops_dom = 2.0 * cfg.N * cfg.D * cfg.V * args.steps
-    per_launch = flops_dom / max(dk["launches"], 1)
+    per_launch = 2.0 * cfg.N * cfg.D * cfg.V * psteps / max(dk["launches"], 1)
     achieved = per_launch / (dk["avg_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -807,10 +871,12 @@ def main():
 
     base = None
     if args.cpu_rows > 0:
-        del H, W, idx, t, ws, dW
+        loss_v = float(loss.item())
+        del H, W, idx, t, ws, dW, dH, lse, loss
         torch.cuda.empty_cache()
-        base = cpu_baseline(inp, cfg, args.cpu_rows)
-        log(f"cpu oracle: {base['value']:.2f} tokens/s on {base['cores']} threads")
+        base = cpu_baseline(inp, cfg, args.cpu_rows, args.cpu_repeats)
+        log(f"cpu oracle: {base['value']:.2f} tokens/s on {base['cores']} threads ({base['cpu_model']}; "
+            f"{base['blas']}); {base['sample']}")
 
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -823,10 +889,30 @@ def main():
         "peak_hbm_gib": round(peak_gib, 3),
         "median_ms": {"step": round(med(step_ms), 4), "forward": round(med(fwd_ms), 4),
                       "backward": round(med(bwd_ms), 4)},
-        "kernel_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in per_kernel.items()},
+        "kernel_ms_per_step": {k: round(v["total_ms"] / psteps, 4) for k, v in per_kernel.items()},
         "roofline": roofline, "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)
+
+
+def load_inputs(cfg, seed, cache_dir=None):
+    """The workload's seeded inputs (synth.make_inputs), optionally through an
+    .npz copy in cache_dir keyed by workload and seed."""
+    import numpy as np
+    from synth import make_inputs
+    path = None
+    if cache_dir:
+        path = os.path.join(cache_dir, f"kd_inputs_{cfg.name}_seed{seed}.npz")
+        if os.path.exists(path):
+            with np.load(path) as z:
+                return {"H": z["H"], "W": z["W"], "idx": z["idx"], "t": z["t"], "cfg": cfg, "seed": seed}
+    inp = make_inputs(cfg, seed)
+    if path is not None:
+        os.makedirs(cache_dir, exist_ok=True)
+        tmp = path + f".{os.getpid()}.tmp.npz"
+        np.savez(tmp, H=inp["H"], W=inp["W"], idx=inp["idx"], t=inp["t"])
+        os.replace(tmp, path)
+    return inp
 
 
 if __name__ == "__main__":

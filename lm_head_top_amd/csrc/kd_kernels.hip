@@ -303,13 +303,22 @@ __device__ __forceinline__ int mn_lane_off(int lane) {
   return (8 * (gq >> 1) + (i16 >> 2)) * 512 + (16 * (gq & 1) + 4 * (i16 & 3)) * 2;
 }
 
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// One ds_read_b64_tr_b16.  The __restrict__ parameter gives the read alias
+// scope information; without it the compiler waits for every direct LDS load
+// in flight (vmcnt(0)) before a transposing read.  The GEMM loops order these
+// reads against the direct loads with their own vmcnt waits and barriers.
+__device__ __forceinline__ s16x4 ds_read_tr(const lds_s16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p));
+}
+
 __device__ __forceinline__ bf16x8 frag_mn(const char* tile, int col0, int s, int lane, int lane_off) {
   // row & 3 of every row this lane addresses equals (lane & 15) >> 2
   const int blk = (col0 >> 5) ^ ((lane & 15) >> 2);
   const char* p = tile + s * (16 * 512) + lane_off + (blk << 6);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  const s16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 4 * 512));
+  const s16x4 lo = ds_read_tr((const lds_s16x4*)(p));
+  const s16x4 hi = ds_read_tr((const lds_s16x4*)(p + 4 * 512));
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }

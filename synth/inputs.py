@@ -83,9 +83,13 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     NaN is mapped to a quiet NaN; the generators never produce one.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    u = x.view(np.uint32)
+    # (u + 0x7FFF + lsb) >> 16 in 32-bit arithmetic: the sum wraps only for
+    # NaN bit patterns (u >= 0xFFFF8001), which are overwritten below
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():

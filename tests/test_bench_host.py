@@ -30,8 +30,8 @@ def _csv(d, counter, entries):
 
 
 def test_traffic_calibration(tmp_path, monkeypatch):
-    out = tmp_path / "traffic.json"
-    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(out))
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
+    out = tmp_path / "traffic_x.json"
     neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>"
     dw = "kd::(anonymous namespace)::dw_kernel(kd::DwArgs)"
     fwd = "void kd::(anonymous namespace)::logits_kernel<0>(kd::LogitsArgs)"
@@ -59,11 +59,11 @@ def test_traffic_calibration(tmp_path, monkeypatch):
 
 
 def test_traffic_needs_copy_kernel(tmp_path, monkeypatch):
-    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tmp_path / "t.json"))
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
     _csv(tmp_path / "f", "FETCH_SIZE", [("dw_kernel", 1.0)])
     _csv(tmp_path / "w", "WRITE_SIZE", [("dw_kernel", 1.0)])
     with pytest.raises(SystemExit):
-        bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"), 64, "", {})
+        bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"), 64, "", {"workload": "x"})
 
 
 def test_kernel_classes():

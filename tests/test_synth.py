@@ -23,6 +23,24 @@ def test_bf16_rne_known_patterns():
     assert f32_to_bf16_bits(big)[0] == 0x7F80
 
 
+def test_bf16_rne_edge_bit_patterns():
+    # largest finite values, infinities, the top of the bit range (where a 32-bit
+    # sum of the rounding bias would wrap) and NaNs: compared with the rounding
+    # written out in 64-bit integers
+    pats = np.concatenate([
+        np.arange(0x7F7F0000, 0x7F810000, 0x1001, dtype=np.uint64),
+        np.arange(0xFF7F0000, 0xFF810000, 0x1001, dtype=np.uint64),
+        np.arange(0xFFFF0000, 0x100000000, 0x111, dtype=np.uint64),
+        np.arange(0x7FFF0000, 0x80010000, 0x777, dtype=np.uint64),
+        np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFFFFFFF], dtype=np.uint64),
+    ]).astype(np.uint32)
+    x = pats.view(np.float32)
+    u = pats.astype(np.uint64)
+    ref = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    ref[np.isnan(x)] = 0x7FC0
+    assert np.array_equal(f32_to_bf16_bits(x), ref)
+
+
 def test_bf16_rne_matches_torch():
     torch = pytest.importorskip("torch")
     x = np.random.default_rng(3).standard_normal(100000).astype(np.float32) * 7
