@@ -30,7 +30,12 @@
  *     and loss 4-byte aligned.  D must be a multiple of 8.
  *   - Limits: 1 <= K <= min(V, KD_MAX_K); 1 <= V <= KD_MAX_V; N >= 0;
  *     chunk >= 1 (a chunk larger than N is clamped to N; the last chunk may be
- *     ragged); T finite and > 0.
+ *     ragged); T finite and > 0.  The GEMMs read their bf16 operands with
+ *     32-bit byte offsets, so V * D and (clamped chunk) * D must stay below
+ *     2^31 - 64 elements; N < 2^31, N * K < 2^31 and D <= 2^20.  Outside these
+ *     the calls return KD_ERR_UNSUPPORTED (and the size queries 0).  Any
+ *     chunk within them is accepted: the gradient GEMMs of a group of chunks
+ *     are split into row blocks whose G rows stay within 32-bit offsets.
  *   - Calls only enqueue work on hip_stream (a hipStream_t, NULL = the null
  *     stream) and return; nothing synchronises the host.  Outputs are valid
  *     when the stream reaches the end of the call.  Asynchronous device

@@ -132,30 +132,73 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _dev_tensor(torch, x, name, dtype, shape=None, device=None, numel=None):
+    """Checks one pointer argument before anything is launched: a contiguous
+    tensor of `dtype` on the GPU `device` (or any GPU when None), of exactly
+    `shape` (a tuple) or `numel` elements.  Raises TypeError for a wrong type
+    or dtype and ValueError for the rest."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {x.dtype})")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got one on {x.device})")
+    if device is not None and x.device != device:
+        raise ValueError(f"{name} is on {x.device}, the other arguments on {device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(x.shape)})")
+    if numel is not None and x.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements (got {x.numel()})")
+    return x
+
+
 def _check_inputs(torch, H, W, idx, t):
-    if not (H.is_cuda and W.is_cuda and idx.is_cuda and t.is_cuda):
-        raise ValueError("H, W, topk_idx and topk_logit must be device tensors")
-    if H.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
-        raise TypeError("H and W must be bfloat16")
-    if idx.dtype != torch.int32 or t.dtype != torch.float32:
-        raise TypeError("topk_idx must be int32 and topk_logit float32")
     for name, x in (("H", H), ("W", W), ("topk_idx", idx), ("topk_logit", t)):
-        if not x.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
     N, D = H.shape
-    V, D2 = W.shape
-    if D2 != D or idx.shape != t.shape or idx.shape[0] != N:
-        raise ValueError("shape mismatch: H[N,D], W[V,D], topk_idx/topk_logit[N,K]")
-    return N, D, V, idx.shape[1]
+    V = W.shape[0]
+    K = idx.shape[1]
+    dev = H.device
+    _dev_tensor(torch, H, "H", torch.bfloat16, (N, D))
+    _dev_tensor(torch, W, "W", torch.bfloat16, (V, D), dev)
+    _dev_tensor(torch, idx, "topk_idx", torch.int32, (N, K), dev)
+    _dev_tensor(torch, t, "topk_logit", torch.float32, (N, K), dev)
+    return N, D, V, K
+
+
+def _check_lse(torch, lse, N, dev, name="lse"):
+    _dev_tensor(torch, lse, name, torch.float32, device=dev, numel=N)
+
+
+def _check_grad_loss(torch, grad_loss, dev):
+    if grad_loss is not None:
+        _dev_tensor(torch, grad_loss, "grad_loss", torch.float32, device=dev, numel=1)
+
+
+def _out_dW(torch, dW, V, D, dev):
+    if dW is None:
+        return torch.zeros((V, D), dtype=torch.float32, device=dev)
+    return _dev_tensor(torch, dW, "dW", torch.float32, (V, D), dev)
+
+
+def _given_workspace(torch, workspace, need, dev, name="workspace"):
+    _dev_tensor(torch, workspace, name, torch.uint8, device=dev)
+    if workspace.dim() != 1 or workspace.numel() < need:
+        raise ValueError(f"{name} must be a 1-D uint8 tensor of at least {need} bytes "
+                         f"(got {workspace.numel()})")
+    return workspace
 
 
 def _workspace(torch, N, D, V, K, chunk, device, workspace):
     need = workspace_size(N, D, V, K, chunk)
     if need == 0:
         raise KDError(1, "workspace_size")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    return workspace
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    return _given_workspace(torch, workspace, need, device)
 
 
 def forward(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024,
@@ -181,17 +224,12 @@ def backward(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0,
     torch = _torch()
     N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
     dev = H.device
-    if lse.dtype != torch.float32 or lse.numel() != N or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [N]")
-    if grad_loss is not None and (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1):
-        raise ValueError("grad_loss must be a float32 device scalar")
+    _check_lse(torch, lse, N, dev)
+    _check_grad_loss(torch, grad_loss, dev)
+    dW = _out_dW(torch, dW, V, D, dev)
     ws = _workspace(torch, N, D, V, K, chunk, dev, workspace)
     dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
-    if dW is None:
-        dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
-    elif dW.dtype != torch.float32 or tuple(dW.shape) != (V, D) or not dW.is_contiguous():
-        raise ValueError("dW must be a contiguous float32 [V, D] tensor")
-    gl = grad_loss.contiguous() if grad_loss is not None else None
+    gl = grad_loss
     st = load_library().kd_topk_kl_backward(
         _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), _ptr(lse), _ptr(gl), N, D, V, K,
         float(T), int(chunk), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
@@ -202,13 +240,11 @@ def backward(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0,
 KD_SCALE_T2 = 1
 
 
-def _ext_args(torch, N, row_weight, labels):
-    if row_weight is not None and (row_weight.dtype != torch.float32 or row_weight.numel() != N
-                                   or not row_weight.is_contiguous() or not row_weight.is_cuda):
-        raise ValueError("row_weight must be a contiguous float32 device tensor [N]")
-    if labels is not None and (labels.dtype != torch.int32 or labels.numel() != N
-                               or not labels.is_contiguous() or not labels.is_cuda):
-        raise ValueError("labels must be a contiguous int32 device tensor [N]")
+def _ext_args(torch, N, row_weight, labels, dev):
+    if row_weight is not None:
+        _dev_tensor(torch, row_weight, "row_weight", torch.float32, device=dev, numel=N)
+    if labels is not None:
+        _dev_tensor(torch, labels, "labels", torch.int32, device=dev, numel=N)
 
 
 def forward_ex(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024, row_weight=None,
@@ -218,8 +254,8 @@ def forward_ex(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024, ro
     cross-entropy term and T^2 scaling.  Returns loss, lse [, row_loss]."""
     torch = _torch()
     N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
-    _ext_args(torch, N, row_weight, labels)
     dev = H.device
+    _ext_args(torch, N, row_weight, labels, dev)
     ws = _workspace(torch, N, D, V, K, chunk, dev, workspace)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
@@ -239,19 +275,14 @@ def backward_ex(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0,
     """dH (overwritten) and dW (accumulated) of the extended loss."""
     torch = _torch()
     N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
-    _ext_args(torch, N, row_weight, labels)
     dev = H.device
-    if lse.dtype != torch.float32 or lse.numel() != N or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [N]")
-    if grad_loss is not None and (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1):
-        raise ValueError("grad_loss must be a float32 device scalar")
+    _ext_args(torch, N, row_weight, labels, dev)
+    _check_lse(torch, lse, N, dev)
+    _check_grad_loss(torch, grad_loss, dev)
+    dW = _out_dW(torch, dW, V, D, dev)
     ws = _workspace(torch, N, D, V, K, chunk, dev, workspace)
     dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
-    if dW is None:
-        dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
-    elif dW.dtype != torch.float32 or tuple(dW.shape) != (V, D) or not dW.is_contiguous():
-        raise ValueError("dW must be a contiguous float32 [V, D] tensor")
-    gl = grad_loss.contiguous() if grad_loss is not None else None
+    gl = grad_loss
     st = load_library().kd_topk_kl_backward_ex(
         _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), _ptr(lse), _ptr(gl), N, D, V, K,
         float(T), int(chunk), _ptr(row_weight), _ptr(labels), float(kd_weight), float(ce_weight),
@@ -275,8 +306,10 @@ def forward_keep(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024,
     need = keep_workspace_size(N, D, V, K, chunk)
     if need == 0:
         raise KDError(1, "keep_workspace_size")
-    if workspace is None or workspace.numel() < need:
+    if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:
+        _given_workspace(torch, workspace, need, dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     row_kl = torch.empty(N, dtype=torch.float32, device=dev) if want_row_kl else None
@@ -292,13 +325,22 @@ def backward_keep(H, W, K: int, workspace, grad_loss=None, T: float = 1.0, chunk
                   dW=None):
     """dH (overwritten) and dW (accumulated) from a forward_keep workspace."""
     torch = _torch()
+    for name, x in (("H", H), ("W", W)):
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
     N, D = H.shape
     V = W.shape[0]
     dev = H.device
+    _dev_tensor(torch, H, "H", torch.bfloat16, (N, D))
+    _dev_tensor(torch, W, "W", torch.bfloat16, (V, D), dev)
+    _check_grad_loss(torch, grad_loss, dev)
+    need = keep_workspace_size(N, D, V, int(K), chunk)
+    if need == 0:
+        raise KDError(1, "keep_workspace_size")
+    _given_workspace(torch, workspace, need, dev)
+    dW = _out_dW(torch, dW, V, D, dev)
     dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
-    if dW is None:
-        dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
-    gl = grad_loss.contiguous() if grad_loss is not None else None
+    gl = grad_loss
     st = load_library().kd_topk_kl_backward_keep(
         _ptr(H), _ptr(W), _ptr(gl), N, D, V, int(K), float(T), int(chunk), _ptr(dH), _ptr(dW),
         _ptr(workspace), workspace.numel(), _stream_ptr(torch, dev))
@@ -307,11 +349,26 @@ def backward_keep(H, W, K: int, workspace, grad_loss=None, T: float = 1.0, chunk
 
 
 def _teacher_dtype(torch, teacher):
+    if not isinstance(teacher, torch.Tensor):
+        raise TypeError("teacher logits must be a torch.Tensor")
     if teacher.dtype == torch.float32:
         return 0
     if teacher.dtype == torch.bfloat16:
         return 1
     raise TypeError("teacher logits must be float32 or bfloat16")
+
+
+def _check_dense(torch, H, W, teacher):
+    for name, x in (("H", H), ("W", W), ("teacher", teacher)):
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
+    N, D = H.shape
+    V = W.shape[0]
+    dev = H.device
+    _dev_tensor(torch, H, "H", torch.bfloat16, (N, D))
+    _dev_tensor(torch, W, "W", torch.bfloat16, (V, D), dev)
+    _dev_tensor(torch, teacher, "teacher", teacher.dtype, (N, V), dev)
+    return N, D, V, _teacher_dtype(torch, teacher)
 
 
 def dense_workspace_size(N: int, D: int, V: int, chunk: int) -> int:
@@ -322,19 +379,16 @@ def _dense_workspace(torch, N, D, V, chunk, device, workspace):
     need = dense_workspace_size(N, D, V, chunk)
     if need == 0:
         raise KDError(1, "dense_workspace_size")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    return workspace
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    return _given_workspace(torch, workspace, need, device)
 
 
 def dense_forward(H, W, teacher, T: float = 1.0, chunk: int = 1024, want_row_kl: bool = False,
                   workspace=None):
     """Dense-teacher KL over the full vocabulary: loss, lse, lse_t [, row_kl]."""
     torch = _torch()
-    N, D = H.shape
-    V = W.shape[0]
-    if tuple(teacher.shape) != (N, V) or not teacher.is_contiguous() or not teacher.is_cuda:
-        raise ValueError("teacher logits must be a contiguous device tensor [N, V]")
+    N, D, V, tdt = _check_dense(torch, H, W, teacher)
     dev = H.device
     ws = _dense_workspace(torch, N, D, V, chunk, dev, workspace)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
@@ -342,7 +396,7 @@ def dense_forward(H, W, teacher, T: float = 1.0, chunk: int = 1024, want_row_kl:
     lse_t = torch.empty(N, dtype=torch.float32, device=dev)
     row_kl = torch.empty(N, dtype=torch.float32, device=dev) if want_row_kl else None
     st = load_library().kd_dense_kl_forward(
-        _ptr(H), _ptr(W), _ptr(teacher), _teacher_dtype(torch, teacher), N, D, V, float(T), int(chunk),
+        _ptr(H), _ptr(W), _ptr(teacher), tdt, N, D, V, float(T), int(chunk),
         _ptr(loss), _ptr(lse), _ptr(lse_t), _ptr(row_kl), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
     _check(st, "kd_dense_kl_forward")
     return (loss, lse, lse_t, row_kl) if want_row_kl else (loss, lse, lse_t)
@@ -352,16 +406,17 @@ def dense_backward(H, W, teacher, lse, lse_t, grad_loss=None, T: float = 1.0, ch
                    dW=None, workspace=None):
     """dH (overwritten) and dW (accumulated) of the dense-teacher KL."""
     torch = _torch()
-    N, D = H.shape
-    V = W.shape[0]
+    N, D, V, tdt = _check_dense(torch, H, W, teacher)
     dev = H.device
+    _check_lse(torch, lse, N, dev)
+    _check_lse(torch, lse_t, N, dev, "lse_t")
+    _check_grad_loss(torch, grad_loss, dev)
+    dW = _out_dW(torch, dW, V, D, dev)
     ws = _dense_workspace(torch, N, D, V, chunk, dev, workspace)
     dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
-    if dW is None:
-        dW = torch.zeros((V, D), dtype=torch.float32, device=dev)
-    gl = grad_loss.contiguous() if grad_loss is not None else None
+    gl = grad_loss
     st = load_library().kd_dense_kl_backward(
-        _ptr(H), _ptr(W), _ptr(teacher), _teacher_dtype(torch, teacher), _ptr(lse), _ptr(lse_t), _ptr(gl),
+        _ptr(H), _ptr(W), _ptr(teacher), tdt, _ptr(lse), _ptr(lse_t), _ptr(gl),
         N, D, V, float(T), int(chunk), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
     _check(st, "kd_dense_kl_backward")
     return dH, dW
@@ -371,14 +426,15 @@ def topk_select(logits, K: int):
     """Teacher top-K cache of fp32 or bf16 logits [N, V]: (ids int32 [N, K],
     logits fp32 [N, K]), best first, equal logits by lower id."""
     torch = _torch()
-    if not logits.is_cuda or logits.dim() != 2 or not logits.is_contiguous():
-        raise ValueError("logits must be a contiguous device tensor [N, V]")
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError("logits must be a 2-D tensor [N, V]")
     if logits.dtype == torch.float32:
         dtype = 0
     elif logits.dtype == torch.bfloat16:
         dtype = 1
     else:
         raise TypeError("logits must be float32 or bfloat16")
+    _dev_tensor(torch, logits, "logits", logits.dtype)
     N, V = logits.shape
     idx = torch.empty((N, K), dtype=torch.int32, device=logits.device)
     val = torch.empty((N, K), dtype=torch.float32, device=logits.device)
@@ -391,6 +447,9 @@ def topk_select(logits, K: int):
 def validate(topk_idx, V: int) -> int:
     """Bit 0: an id outside [0, V); bit 1: a repeated id within a row."""
     torch = _torch()
+    if not isinstance(topk_idx, torch.Tensor) or topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be a 2-D tensor [N, K]")
+    _dev_tensor(torch, topk_idx, "topk_idx", torch.int32)
     N, K = topk_idx.shape
     flags = torch.empty(1, dtype=torch.int32, device=topk_idx.device)
     st = load_library().kd_topk_kl_validate(_ptr(topk_idx), N, K, V, _ptr(flags),

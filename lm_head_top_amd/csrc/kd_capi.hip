@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -68,7 +69,12 @@ bool bad_ptr(const void* p, size_t align) { return p == nullptr || !kd::aligned(
 extern "C" {
 
 const char* kd_status_string(kd_status s) {
-  switch (s) {
+  // A C caller may pass any int; in C++ an enum value outside the
+  // enumerators' range is undefined, so read the bits as an int.
+  static_assert(sizeof(kd_status) == sizeof(int), "kd_status is an int");
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case KD_OK:
       return "ok";
     case KD_ERR_INVALID_ARG:
@@ -302,8 +308,13 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
           KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
                     kd::launch_dh_reduce(dhp, p.grp_split, brows, int(D), p.grp_pad, dHb, s));
       }
-      kd::DwArgs wa{G, H + group_row0 * D, grows, int(D), int(V), p.Vp, dW};
-      KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
+      // dW += G^T H over the group, in row blocks of at most gemm_rows (one
+      // block unless G's rows outgrow 32-bit offsets); each block adds once
+      for (int64_t b0 = 0; b0 < grows; b0 += p.gemm_rows) {
+        const int brows = int(grows - b0 < p.gemm_rows ? grows - b0 : p.gemm_rows);
+        kd::DwArgs wa{G + b0 * p.Vp, H + (group_row0 + b0) * D, brows, int(D), int(V), p.Vp, dW};
+        KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
+      }
       gj = 0;
     }
   }
@@ -383,8 +394,10 @@ kd_status kd_topk_kl_backward_keep(const uint16_t* H, const uint16_t* W, const f
   float* dhp = reinterpret_cast<float*>(ws + kp.off_dhp);
   const int ktiles = int(p.Vp / kd::gemm_bk());
   const int kps = (ktiles + p.dh_split - 1) / p.dh_split;
-  for (int64_t row0 = 0; row0 < N; row0 += p.chunk) {
-    const int rows = int(N - row0 < p.chunk ? N - row0 : p.chunk);
+  // dH in blocks of one chunk (or fewer rows when a chunk of G outgrows 32-bit offsets)
+  const int64_t hstep = p.chunk < p.gemm_rows ? p.chunk : p.gemm_rows;
+  for (int64_t row0 = 0; row0 < N; row0 += hstep) {
+    const int rows = int(N - row0 < hstep ? N - row0 : hstep);
     kd::DhArgs da{gall + row0 * p.Vp, W, rows, int(D), int(V), p.Vp, p.dh_split, kps, dhp, dH + row0 * D,
                   p.c_pad, grad_loss};
     KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));

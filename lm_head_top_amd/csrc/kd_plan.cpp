@@ -65,15 +65,22 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
   p.npt = p.c_pad / kTile;
   p.dh_split = dh_split_for(c, D);
   p.dw_group = dw_group_for(c, N);
-  const int64_t dh_rows = p.dw_group * c < kDhRows ? p.dw_group * c : kDhRows;
+  // Every bf16 GEMM operand is read through a buffer descriptor with 32-bit
+  // byte offsets: W [V, D] whole, a chunk's H rows [c, D] in the logits GEMMs,
+  // and in dH / dW a block of G rows [rows, Vp] and H rows [rows, D].  W and
+  // a chunk of H must fit; the gradient GEMMs of a group are split into row
+  // blocks of at most gemm_rows.  (G is written and dW accumulated through
+  // 64-bit addresses.)
+  constexpr int64_t kLim = (int64_t(1) << 31) - 64;  // elements
+  if (V * D > kLim || p.Vp * D > kLim || c * D > kLim) return KD_ERR_UNSUPPORTED;
+  int64_t gr = kLim / p.Vp;
+  if (kLim / D < gr) gr = kLim / D;
+  p.gemm_rows = gr / kTile * kTile;
+  if (p.gemm_rows < kTile) return KD_ERR_UNSUPPORTED;
+  int64_t dh_rows = p.dw_group * c < kDhRows ? p.dw_group * c : kDhRows;
+  if (dh_rows > p.gemm_rows) dh_rows = p.gemm_rows;
   p.grp_pad = ceil_div(dh_rows, kTile) * kTile;
   p.grp_split = dh_split_for(dh_rows, D);
-  // every GEMM operand is addressed with 32-bit buffer offsets (bf16)
-  if (p.dw_group * c * p.Vp > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
-  if (p.dw_group * c * D > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
-  if (V * D > (int64_t(1) << 31) - 64 || p.Vp * D > (int64_t(1) << 31) - 64) return KD_ERR_UNSUPPORTED;
-  // the fp32 dW accumulator is read through a buffer descriptor as well
-  if (V * D * 4 > (int64_t(1) << 32) - 64) return KD_ERR_UNSUPPORTED;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -128,13 +135,8 @@ kd_status make_keep_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, in
   kp.off_gall = take(size_t(N > 0 ? N : 1) * p.Vp * 2);
   kp.off_dhp = take(p.dh_split > 1 ? size_t(p.dh_split) * p.c_pad * D * 4 : 0);
   kp.bytes = off;
-  // rows per dW GEMM: G and H are addressed with 32-bit offsets from the group's first row
-  const int64_t lim = (int64_t(1) << 31) - 64;
-  int64_t L = lim / (p.Vp * 2);
-  if (lim / (D * 2) < L) L = lim / (D * 2);
-  L = L / kTile * kTile;
-  if (L < kTile) return KD_ERR_UNSUPPORTED;
-  kp.dw_rows = N < L ? (N > 0 ? N : 1) : L;
+  // rows per dW GEMM: G and H are addressed with 32-bit offsets from the block's first row
+  kp.dw_rows = N < p.gemm_rows ? (N > 0 ? N : 1) : p.gemm_rows;
   *plan = kp;
   return KD_OK;
 }

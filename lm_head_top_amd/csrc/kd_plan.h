@@ -26,7 +26,10 @@ struct Plan {
   int64_t npt = 0;     // position tiles per chunk
   int dh_split = 1;    // split-K factor of a dH GEMM over one chunk (the kept-gradient comparator)
   int dw_group = 1;    // consecutive chunks whose G rows feed one dW GEMM (K = dw_group * chunk)
-  int64_t grp_pad = 0; // rows of one dH GEMM over a group: min(group rows, kDhRows), rounded up to kTile
+  int64_t gemm_rows = 0; // most rows of G (and H) one dH or dW GEMM may take: its operands are
+                         // addressed with 32-bit buffer offsets (rows * Vp and rows * D below 2^31
+                         // elements); a group's GEMMs are split into row blocks of at most this
+  int64_t grp_pad = 0; // rows of one dH GEMM over a group: min(group rows, kDhRows, gemm_rows), rounded up to kTile
   int grp_split = 1;   // split-K factor of such a dH GEMM
   // The teacher probabilities and the id buckets are formed for a group of
   // dw_group chunks at once: chunk j of a group has its p and h rows at

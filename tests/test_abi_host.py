@@ -84,6 +84,21 @@ def test_workspace_size_rejects(lib):
     assert f(0, 16, 100, 5, 4) > 0            # empty batch is valid
 
 
+def test_workspace_size_limits_of_32bit_operand_offsets(lib):
+    f = kd.workspace_size
+    # a chunk whose G rows exceed 2^31 elements is accepted (its gradient GEMMs
+    # run in row blocks): 16384 x 131072 bf16 is 4 GiB of G
+    big = f(32768, 4096, 131072, 100, 16384)
+    assert big >= 16384 * 131072 * 2
+    assert f(4096, 64, 1 << 20, 8, 4096) >= 4096 * (1 << 20) * 2
+    # W [V, D] and one chunk of H [chunk, D] are read whole through 32-bit offsets
+    assert f(16, 8192, (1 << 18) + 256, 5, 16) == 0      # V * D > 2^31 - 64
+    assert f(1 << 20, 4096, 1024, 5, 1 << 19) == 0        # chunk * D > 2^31 - 64
+    assert f(1 << 20, 4096, 1024, 5, (1 << 19) - 256) > 0
+    assert f(16, 4096, 1 << 19, 5, 16) == 0                # V * D = 2^31
+    assert f(16, 4096, (1 << 19) - 256, 5, 16) > 0
+
+
 def _fwd(lib, **kw):
     a = dict(H=8192 * 16, W=8192 * 16, idx=1 << 20, t=1 << 21, N=4, D=16, V=64, K=3, T=1.0,
              chunk=2, loss=1 << 22, lse=1 << 23, row_kl=0, ws=1 << 24, ws_bytes=1 << 30, stream=0)
