@@ -116,6 +116,31 @@ kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W,
                              void* hip_stream);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as kd_topk_kl_forward
+ * without the workspace: its scratch is a 64 MiB array the library holds in
+ * device memory on each GPU it runs on, until the process ends.  Nothing is
+ * allocated or freed by the call.
+ *   - Problems whose forward workspace region exceeds 64 MiB return
+ *     KD_ERR_WORKSPACE before any HIP call.  The region is O(chunk * V / 256
+ *     + R * K + N) bytes (R: rows of a group of chunks, see
+ *     kd_topk_kl_workspace_size): 25 MiB at N = 262144, V = 131072,
+ *     chunk = 4096 and 42 MiB at chunk 8192; chunk 16384 at V = 131072
+ *     (83 MiB) does not fit.
+ *   - Every call on one GPU uses that GPU's single array: calls that overlap
+ *     on one GPU (other streams, other host threads) race and give undefined
+ *     results.  Calls on different GPUs are independent.
+ *   - The first call on a device looks the array up (hipGetSymbolAddress);
+ *     that call's HIP errors return KD_ERR_HIP.
+ */
+kd_status kd_topk_kl_forward_noalloc(const uint16_t* H, const uint16_t* W,
+                                     const int32_t* topk_idx, const float* topk_logit,
+                                     int64_t N, int64_t D, int64_t V, int32_t K, float T,
+                                     int64_t chunk, float* loss, float* lse, float* row_kl,
+                                     void* hip_stream);
+
+/*
  * Backward pass (same section: the backward recomputes every chunk's
  * logits instead of keeping them, so the projection runs twice).
  *

@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = [
-    "lib_path", "load_library", "workspace_size", "forward", "backward", "validate",
+    "lib_path", "load_library", "workspace_size", "forward", "forward_noalloc", "backward", "validate",
     "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError", "topk_select",
     "keep_workspace_size", "forward_keep", "backward_keep",
     "dense_workspace_size", "dense_forward", "dense_backward", "forward_ex", "backward_ex",
@@ -67,6 +67,9 @@ def load_library():
     lib.kd_topk_kl_forward.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_f,
                                        c_i64, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
     lib.kd_topk_kl_forward.restype = ctypes.c_int
+    lib.kd_topk_kl_forward_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_f,
+                                               c_i64, c_vp, c_vp, c_vp, c_vp]
+    lib.kd_topk_kl_forward_noalloc.restype = ctypes.c_int
     lib.kd_topk_kl_backward.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                         c_i32, c_f, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]
     lib.kd_topk_kl_backward.restype = ctypes.c_int
@@ -216,6 +219,30 @@ def forward(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024,
         _ptr(loss), _ptr(lse), _ptr(row_kl), _ptr(ws), ws.numel(), _stream_ptr(torch, dev))
     _check(st, "kd_topk_kl_forward")
     return (loss, lse, row_kl) if want_row_kl else (loss, lse)
+
+
+def forward_noalloc(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024,
+                    want_row_kl: bool = False, loss=None, lse=None, row_kl=None):
+    """kd_topk_kl_forward_noalloc: the forward with the library's own device
+    scratch instead of a workspace (the library allocates nothing).  Outputs
+    may be passed in (loss fp32 [1], lse fp32 [N], row_kl fp32 [N]) so the
+    call allocates nothing here either; missing ones are created."""
+    torch = _torch()
+    N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
+    dev = H.device
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else \
+        _dev_tensor(torch, loss, "loss", torch.float32, device=dev, numel=1)
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else \
+        _dev_tensor(torch, lse, "lse", torch.float32, device=dev, numel=N)
+    if want_row_kl and row_kl is None:
+        row_kl = torch.empty(N, dtype=torch.float32, device=dev)
+    elif row_kl is not None:
+        _dev_tensor(torch, row_kl, "row_kl", torch.float32, device=dev, numel=N)
+    st = load_library().kd_topk_kl_forward_noalloc(
+        _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), N, D, V, K, float(T), int(chunk),
+        _ptr(loss), _ptr(lse), _ptr(row_kl), _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_forward_noalloc")
+    return (loss, lse, row_kl) if row_kl is not None else (loss, lse)
 
 
 def backward(H, W, topk_idx, topk_logit, lse, grad_loss=None, T: float = 1.0,

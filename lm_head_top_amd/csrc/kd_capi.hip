@@ -321,18 +321,61 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
   return KD_OK;
 }
 
-kd_status check_forward_args(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
-                             const float* topk_logit, int64_t N, float* loss, float* lse, float* row_kl,
-                             void* workspace, size_t workspace_bytes, size_t need) {
+kd_status check_forward_ptrs(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                             const float* topk_logit, int64_t N, float* loss, float* lse, float* row_kl) {
   if (bad_ptr(loss, 4)) return KD_ERR_INVALID_ARG;
   if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(topk_idx, 4) ||
                 bad_ptr(topk_logit, 4) || bad_ptr(lse, 4)))
     return KD_ERR_INVALID_ARG;
   if (row_kl != nullptr && !kd::aligned(row_kl, 4)) return KD_ERR_INVALID_ARG;
+  return KD_OK;
+}
+
+kd_status check_forward_args(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                             const float* topk_logit, int64_t N, float* loss, float* lse, float* row_kl,
+                             void* workspace, size_t workspace_bytes, size_t need) {
+  const kd_status st = check_forward_ptrs(H, W, topk_idx, topk_logit, N, loss, lse, row_kl);
+  if (st != KD_OK) return st;
   if (N > 0 && (workspace == nullptr || workspace_bytes < need)) return KD_ERR_WORKSPACE;
   if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
   (void)p;
   return KD_OK;
+}
+
+}  // namespace
+
+// ---- allocation-free forward: its scratch is a file-scope device array ----
+
+// Size of the array; kd_topk_kl_forward_noalloc rejects problems whose
+// forward workspace region is larger.  Each GPU the library runs on holds one
+// copy until the process ends.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+
+// Device address of `scratch` per device.  In host code the array's name is
+// a host-side stand-in, not a device address, so kernels get this pointer.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Looks up the current device's copy of `scratch` on its first use there.
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || !kd::aligned(ptr, 256)) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -346,6 +389,31 @@ kd_status kd_topk_kl_forward(const uint16_t* H, const uint16_t* W, const int32_t
   // the extended loss at its neutral settings: no weights, no labels, kd_weight 1
   return kd_topk_kl_forward_ex(H, W, topk_idx, topk_logit, N, D, V, K, T, chunk, nullptr, nullptr, 1.f, 0.f, 0,
                                loss, lse, row_kl, workspace, workspace_bytes, hip_stream);
+}
+
+kd_status kd_topk_kl_forward_noalloc(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                     const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                                     float T, int64_t chunk, float* loss, float* lse, float* row_kl,
+                                     void* hip_stream) {
+  kd::Plan p;
+  kd_status st = kd::make_plan(N, D, V, K, T, chunk, &p);
+  if (st != KD_OK) return st;
+  st = check_forward_ptrs(H, W, topk_idx, topk_logit, N, loss, lse, row_kl);
+  if (st != KD_OK) return st;
+  if (p.fwd_bytes > kNoallocScratchBytes) return KD_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (N == 0) {
+    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
+    return KD_OK;
+  }
+  void* ws = nullptr;
+  const hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) return hip_failed(e);
+  // nothing in the scratch has to start at zero: with ids in [0, V) every
+  // forward buffer is written before it is read within the call (other ids
+  // give unspecified results, as with a caller's workspace)
+  return run_forward(p, H, W, topk_idx, topk_logit, N, D, V, K, T, loss, lse, row_kl, static_cast<char*>(ws),
+                     nullptr, nullptr, s);
 }
 
 size_t kd_topk_kl_keep_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int64_t chunk) {

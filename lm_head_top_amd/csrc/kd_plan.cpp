@@ -112,6 +112,7 @@ kd_status make_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t
   // fp32 split-K partials of one dH GEMM
   p.off_dhp = take(p.grp_split > 1 ? size_t(p.grp_split) * p.grp_pad * D * 4 : 0);
   const size_t bwd_end = off;
+  p.fwd_bytes = fwd_end;
   p.bytes = fwd_end > bwd_end ? fwd_end : bwd_end;
   *plan = p;
   return KD_OK;

@@ -41,6 +41,7 @@ struct Plan {
   size_t off_p = 0, off_h = 0, off_boff = 0, off_ent = 0, off_scalar = 0;  // shared by fwd and bwd
   size_t off_pm = 0, off_ps = 0, off_zsel = 0, off_rowkl = 0;  // forward only
   size_t off_g = 0, off_dhp = 0;  // backward only (aliases forward); dhp: [grp_split, grp_pad, D]
+  size_t fwd_bytes = 0;  // the part of the workspace the forward uses (shared and forward-only regions)
   size_t bytes = 0;
 };
 

@@ -162,6 +162,32 @@ def test_backward_rejects_before_any_hip_call(lib, kw, want):
     assert _bwd(lib, **kw) == want
 
 
+def _fwd_noalloc(lib, **kw):
+    a = dict(H=8192 * 16, W=8192 * 16, idx=1 << 20, t=1 << 21, N=4, D=16, V=64, K=3, T=1.0,
+             chunk=2, loss=1 << 22, lse=1 << 23, row_kl=0, stream=0)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return lib.kd_topk_kl_forward_noalloc(v(a["H"]), v(a["W"]), v(a["idx"]), v(a["t"]), a["N"], a["D"],
+                                          a["V"], a["K"], a["T"], a["chunk"], v(a["loss"]), v(a["lse"]),
+                                          v(a["row_kl"]), v(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(H=0), KD_ERR_INVALID_ARG),
+    (dict(loss=0), KD_ERR_INVALID_ARG),
+    (dict(lse=0), KD_ERR_INVALID_ARG),
+    (dict(idx=(1 << 20) + 2), KD_ERR_INVALID_ARG),
+    (dict(T=0.0), KD_ERR_INVALID_ARG),
+    (dict(K=65), KD_ERR_INVALID_ARG),
+    (dict(V=(1 << 20) + 8), KD_ERR_UNSUPPORTED),
+    # forward scratch beyond the library's 64 MiB array: 512 vocab tiles x
+    # 16384 positions of (max, sum exp) partials alone take 64 MiB
+    (dict(N=32768, D=64, V=131072, K=4, chunk=16384), KD_ERR_WORKSPACE),
+])
+def test_forward_noalloc_rejects_before_any_hip_call(lib, kw, want):
+    assert _fwd_noalloc(lib, **kw) == want
+
+
 def test_backward_empty_batch_is_a_no_op(lib):
     # N = 0: nothing to accumulate, nothing enqueued
     assert _bwd(lib, N=0, H=0, W=0, idx=0, t=0, lse=0, dH=0, ws=0, ws_bytes=0) == KD_OK
