@@ -329,6 +329,8 @@ def dense_reference(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(0)
     cfg = get_config(args.config)
+    if args.dense_n > 0:
+        cfg = cfg.replace(N=args.dense_n)
     inp = make_inputs(cfg, args.seed)
     H = torch.from_numpy(inp["H"].view(np.int16)).view(torch.bfloat16).to(dev)
     W = torch.from_numpy(inp["W"].view(np.int16)).view(torch.bfloat16).to(dev)
@@ -430,9 +432,12 @@ def topk_writer(args):
 
 def keep_compare(args):
     """The fused loss (recomputes each chunk in the backward, 8 N D V flops,
-    O(chunk V) memory) beside the kept-gradient comparator (keeps G for the
-    backward, 6 N D V flops, O(N V) memory) on the same inputs: time of one
-    forward + backward and peak memory.  A measurement aid."""
+    O(chunk V) memory) beside the comparators that keep instead of
+    recomputing, on the same inputs: kept gradient (bf16 G for all N, 6 N D V
+    flops) and kept logits (every chunk's fp32 logits, the pages' next-best
+    variant, 6 N D V flops).  Each mode runs on its own, with the device
+    memory of the previous one released: time of one forward + backward
+    (median of --steps) and peak memory.  A measurement aid."""
     import torch
     import lm_head_top_amd as kd
     from synth import get_config
@@ -452,13 +457,20 @@ def keep_compare(args):
         kd.backward(H, W, idx, t, lse, None, T, chunk, dW=dW)
         return loss
 
-    def keep():
+    def keep_grad():
         loss, lse, ws = kd.forward_keep(H, W, idx, t, T, chunk)
         kd.backward_keep(H, W, K, ws, None, T, chunk, dW=dW)
         return loss
 
+    def keep_logits():
+        loss, lse, ws = kd.forward_keep_logits(H, W, idx, t, T, chunk)
+        kd.backward_keep_logits(H, W, idx, t, lse, ws, None, T, chunk, dW=dW)
+        return loss
+
+    modes = {"fused": fused, "kept_gradient": keep_grad, "kept_logits": keep_logits}
     out = {}
-    for name, fn in (("fused", fused), ("kept_gradient", keep)):
+    for name in args.keep_modes:
+        fn = modes[name]
         fn()
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -476,11 +488,17 @@ def keep_compare(args):
                      "peak_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
                      "loss": float(loss.item())}
         log(f"{name}: {out[name]}")
-    line = {"mode": "kept_gradient_compare",
+        del loss
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    line = {"mode": "keep_compare",
             "config": {"workload": WORKLOAD_NAMES[cfg.name], "N": N, "D": D, "V": V, "K": K,
                        "chunk": chunk, "seed": args.seed}, **out,
-            "time_ratio_fused_over_kept": round(out["fused"]["ms_median"] / out["kept_gradient"]["ms_median"], 3),
-            "memory_ratio_kept_over_fused": round(out["kept_gradient"]["peak_gib"] / out["fused"]["peak_gib"], 3)}
+            "dense_grid_fp32_gib": round(N * V * 4 / 2**30, 3)}
+    for name in out:
+        if name != "fused" and "fused" in out:
+            line[f"time_ratio_{name}_over_fused"] = round(out[name]["ms_median"] / out["fused"]["ms_median"], 3)
+            line[f"memory_ratio_{name}_over_fused"] = round(out[name]["peak_gib"] / out["fused"]["peak_gib"], 3)
     print(json.dumps(line), flush=True)
 
 
@@ -717,7 +735,11 @@ def main():
                     help="time the teacher top-K cache writer on N x V teacher logits of --config")
     ap.add_argument("--topk-dtype", default="f32", choices=("f32", "bf16"))
     ap.add_argument("--keep-compare", action="store_true",
-                    help="the fused loss beside the kept-gradient comparator on --config")
+                    help="the fused loss beside the kept-gradient and kept-logits comparators on --config")
+    ap.add_argument("--keep-modes", nargs="+", default=["fused", "kept_gradient", "kept_logits"],
+                    choices=["fused", "kept_gradient", "kept_logits"])
+    ap.add_argument("--dense-n", type=int, default=0,
+                    help="with --dense-reference: positions to use instead of the workload's N")
     ap.add_argument("--dense-teacher", action="store_true",
                     help="the dense-teacher (full-vocabulary) mode on --config "
                          "(teacher dtype from --topk-dtype)")

@@ -228,6 +228,38 @@ kd_status kd_topk_kl_backward_keep(const uint16_t* H, const uint16_t* W, const f
                                    void* hip_stream);
 
 /*
+ * Kept-logits comparator: the pages' next-best variant, which chunks the
+ * forward but keeps each chunk's logits for the backward instead of
+ * recomputing them ("Distilling an LLM on One GPU", section "The two
+ * changes": it reaches 134.2 GiB at 256K tokens against 11.6 GiB for the
+ * fully chunked loss; "Breaking the Memory Barrier", section "Supporting
+ * Context and Metrics").  Same loss and gradients as kd_topk_kl_forward /
+ * kd_topk_kl_backward, 6 N D V flops instead of 8, memory O(N V):
+ *
+ *   kd_topk_kl_forward_keep_logits   as kd_topk_kl_forward, and it also
+ *                                    leaves z = (H W^T)/T for all N positions
+ *                                    (fp32 [N, Vp], Vp = V rounded up to 256)
+ *                                    in the workspace;
+ *   kd_topk_kl_backward_keep_logits  as kd_topk_kl_backward, forming each
+ *                                    chunk's G from the kept logits (which it
+ *                                    overwrites: one backward per forward).
+ *
+ * The workspace (kd_topk_kl_keep_logits_workspace_size bytes, 256-byte
+ * aligned, caller-owned) must be the one the forward filled, with the same
+ * sizes: kd_topk_kl_workspace_size plus N * Vp * 4 bytes.
+ */
+size_t kd_topk_kl_keep_logits_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int64_t chunk);
+kd_status kd_topk_kl_forward_keep_logits(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                         const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                                         float T, int64_t chunk, float* loss, float* lse, float* row_kl,
+                                         void* workspace, size_t workspace_bytes, void* hip_stream);
+kd_status kd_topk_kl_backward_keep_logits(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                          const float* topk_logit, const float* lse, const float* grad_loss,
+                                          int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                                          uint16_t* dH, float* dW, void* workspace, size_t workspace_bytes,
+                                          void* hip_stream);
+
+/*
  * Dense-teacher (online) mode: the same fused loss with the teacher's full-
  * vocabulary logits streamed chunk by chunk instead of a top-K cache, i.e.
  * KL(softmax(t/T) || softmax(z/T)) over all V entries (the online

@@ -16,6 +16,7 @@ __all__ = [
     "lib_path", "load_library", "workspace_size", "forward", "forward_noalloc", "backward", "validate",
     "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError", "topk_select",
     "keep_workspace_size", "forward_keep", "backward_keep",
+    "keep_logits_workspace_size", "forward_keep_logits", "backward_keep_logits",
     "dense_workspace_size", "dense_forward", "dense_backward", "forward_ex", "backward_ex",
 ]
 
@@ -91,6 +92,12 @@ def load_library():
     lib.kd_topk_kl_backward_keep.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_f, c_i64,
                                              c_vp, c_vp, c_vp, c_sz, c_vp]
     lib.kd_topk_kl_backward_keep.restype = ctypes.c_int
+    lib.kd_topk_kl_keep_logits_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i64]
+    lib.kd_topk_kl_keep_logits_workspace_size.restype = c_sz
+    lib.kd_topk_kl_forward_keep_logits.argtypes = lib.kd_topk_kl_forward.argtypes
+    lib.kd_topk_kl_forward_keep_logits.restype = ctypes.c_int
+    lib.kd_topk_kl_backward_keep_logits.argtypes = lib.kd_topk_kl_backward.argtypes
+    lib.kd_topk_kl_backward_keep_logits.restype = ctypes.c_int
     lib.kd_dense_kl_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64]
     lib.kd_dense_kl_workspace_size.restype = c_sz
     lib.kd_dense_kl_forward.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_f, c_i64,
@@ -372,6 +379,57 @@ def backward_keep(H, W, K: int, workspace, grad_loss=None, T: float = 1.0, chunk
         _ptr(H), _ptr(W), _ptr(gl), N, D, V, int(K), float(T), int(chunk), _ptr(dH), _ptr(dW),
         _ptr(workspace), workspace.numel(), _stream_ptr(torch, dev))
     _check(st, "kd_topk_kl_backward_keep")
+    return dH, dW
+
+
+def keep_logits_workspace_size(N: int, D: int, V: int, K: int, chunk: int) -> int:
+    return int(load_library().kd_topk_kl_keep_logits_workspace_size(N, D, V, K, chunk))
+
+
+def forward_keep_logits(H, W, topk_idx, topk_logit, T: float = 1.0, chunk: int = 1024,
+                        want_row_kl: bool = False, workspace=None):
+    """Kept-logits comparator: the forward's outputs plus the workspace holding
+    every chunk's fp32 logits, which backward_keep_logits consumes.  Returns
+    (loss, lse[, row_kl], workspace)."""
+    torch = _torch()
+    N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
+    dev = H.device
+    need = keep_logits_workspace_size(N, D, V, K, chunk)
+    if need == 0:
+        raise KDError(1, "keep_logits_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:
+        _given_workspace(torch, workspace, need, dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(N, dtype=torch.float32, device=dev) if want_row_kl else None
+    st = load_library().kd_topk_kl_forward_keep_logits(
+        _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), N, D, V, K, float(T), int(chunk),
+        _ptr(loss), _ptr(lse), _ptr(row_kl), _ptr(workspace), workspace.numel(), _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_forward_keep_logits")
+    return ((loss, lse, row_kl) if want_row_kl else (loss, lse)) + (workspace,)
+
+
+def backward_keep_logits(H, W, topk_idx, topk_logit, lse, workspace, grad_loss=None, T: float = 1.0,
+                         chunk: int = 1024, dW=None):
+    """dH (overwritten) and dW (accumulated) from a forward_keep_logits
+    workspace (its kept logits are consumed)."""
+    torch = _torch()
+    N, D, V, K = _check_inputs(torch, H, W, topk_idx, topk_logit)
+    dev = H.device
+    _check_lse(torch, lse, N, dev)
+    _check_grad_loss(torch, grad_loss, dev)
+    need = keep_logits_workspace_size(N, D, V, K, chunk)
+    if need == 0:
+        raise KDError(1, "keep_logits_workspace_size")
+    _given_workspace(torch, workspace, need, dev)
+    dW = _out_dW(torch, dW, V, D, dev)
+    dH = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    st = load_library().kd_topk_kl_backward_keep_logits(
+        _ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logit), _ptr(lse), _ptr(grad_loss), N, D, V, K,
+        float(T), int(chunk), _ptr(dH), _ptr(dW), _ptr(workspace), workspace.numel(), _stream_ptr(torch, dev))
+    _check(st, "kd_topk_kl_backward_keep_logits")
     return dH, dW
 
 

@@ -141,11 +141,13 @@ kd_status prepare_group(const kd::Plan& p, const int32_t* topk_idx, const float*
 }
 
 // The forward's chunk loop.  With zkeep / gall set (kept-gradient mode) each
-// chunk's fp32 logits are kept and turned into its G rows of gall.
+// chunk's fp32 logits are kept and turned into its G rows of gall.  With
+// zall set (kept-logits mode) every chunk's fp32 logits are kept in zall
+// [N, Vp] for the backward.
 kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
                       const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K, float T,
                       float* loss, float* lse, float* row_kl, char* ws, float* zkeep, uint16_t* gall,
-                      hipStream_t s, const LossExt& ext = LossExt()) {
+                      hipStream_t s, const LossExt& ext = LossExt(), float* zall = nullptr) {
   float* pw = reinterpret_cast<float*>(ws + p.off_p);
   float* hw = reinterpret_cast<float*>(ws + p.off_h);
   int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
@@ -187,7 +189,7 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
     la.invT = invT;
     la.boff = boffc;
     la.ent = entc;
-    la.zkeep = zkeep;
+    la.zkeep = zall != nullptr ? zall + row0 * p.Vp : zkeep;
     la.pm = pm;
     la.ps = ps;
     la.zsel = zsel;
@@ -227,7 +229,7 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
                        const float* topk_logit, const void* tlog, int t_dtype, const float* lse,
                        const float* lse_t, const float* grad_loss, int64_t N, int64_t D, int64_t V,
                        int32_t K, float T, uint16_t* dH, float* dW, char* ws, hipStream_t s,
-                       const LossExt& ext = LossExt()) {
+                       const LossExt& ext = LossExt(), float* zall = nullptr) {
   float* pw = reinterpret_cast<float*>(ws + p.off_p);
   float* hw = reinterpret_cast<float*>(ws + p.off_h);
   int32_t* boff = reinterpret_cast<int32_t*>(ws + p.off_boff);
@@ -293,7 +295,16 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
     la.alpha = ext.alpha;
     la.beta = ext.beta;
     la.G = Gc;
-    KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
+    if (zall != nullptr) {
+      // kept-logits mode: G_c = bf16((softmax - p scattered) / (N T)) from the
+      // chunk's fp32 logits the forward kept (overwritten); grad_loss scales
+      // the dH and dW GEMMs below
+      KD_LAUNCH(KD_KERNEL_KEEP_GRAD, s,
+                kd::launch_keep_grad(zall + row0 * p.Vp, lse + row0, topk_idx + row0 * K, la.p, rows, K,
+                                     int(V), p.Vp, float(1.0 / (double(N) * double(T))), Gc, s));
+    } else {
+      KD_LAUNCH(KD_KERNEL_LOGITS_BWD, s, kd::launch_logits_bwd(la, s));
+    }
     ++gj;
     const bool last = row0 + p.chunk >= N;
     if (gj == p.dw_group || last) {
@@ -302,7 +313,8 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
       for (int64_t b0 = 0; b0 < grows; b0 += p.grp_pad) {
         const int brows = int(grows - b0 < p.grp_pad ? grows - b0 : p.grp_pad);
         uint16_t* dHb = dH + (group_row0 + b0) * D;
-        kd::DhArgs da{G + b0 * p.Vp, W, brows, int(D), int(V), p.Vp, p.grp_split, kps, dhp, dHb, p.grp_pad};
+        kd::DhArgs da{G + b0 * p.Vp, W,          brows,      int(D), int(V), p.Vp, p.grp_split, kps, dhp, dHb,
+                      p.grp_pad,         zall != nullptr ? grad_loss : nullptr};
         KD_LAUNCH(KD_KERNEL_DH, s, kd::launch_dh(da, s));
         if (p.grp_split > 1)
           KD_LAUNCH(KD_KERNEL_DH_REDUCE, s,
@@ -312,7 +324,8 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
       // block unless G's rows outgrow 32-bit offsets); each block adds once
       for (int64_t b0 = 0; b0 < grows; b0 += p.gemm_rows) {
         const int brows = int(grows - b0 < p.gemm_rows ? grows - b0 : p.gemm_rows);
-        kd::DwArgs wa{G + b0 * p.Vp, H + (group_row0 + b0) * D, brows, int(D), int(V), p.Vp, dW};
+        kd::DwArgs wa{G + b0 * p.Vp, H + (group_row0 + b0) * D, brows, int(D), int(V), p.Vp, dW,
+                      zall != nullptr ? grad_loss : nullptr};
         KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
       }
       gj = 0;
@@ -479,6 +492,54 @@ kd_status kd_topk_kl_backward_keep(const uint16_t* H, const uint16_t* W, const f
     KD_LAUNCH(KD_KERNEL_DW, s, kd::launch_dw(wa, s));
   }
   return KD_OK;
+}
+
+size_t kd_topk_kl_keep_logits_workspace_size(int64_t N, int64_t D, int64_t V, int32_t K, int64_t chunk) {
+  kd::KeepLogitsPlan kp;
+  if (kd::make_keep_logits_plan(N, D, V, K, 1.f, chunk, &kp) != KD_OK) return 0;
+  return kp.bytes;
+}
+
+kd_status kd_topk_kl_forward_keep_logits(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                         const float* topk_logit, int64_t N, int64_t D, int64_t V, int32_t K,
+                                         float T, int64_t chunk, float* loss, float* lse, float* row_kl,
+                                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+  kd::KeepLogitsPlan kp;
+  kd_status st = kd::make_keep_logits_plan(N, D, V, K, T, chunk, &kp);
+  if (st != KD_OK) return st;
+  st = check_forward_args(kp.base, H, W, topk_idx, topk_logit, N, loss, lse, row_kl, workspace,
+                          workspace_bytes, kp.bytes);
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (N == 0) {
+    KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_fill_f32(loss, 1, 0.f, s));
+    return KD_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  return run_forward(kp.base, H, W, topk_idx, topk_logit, N, D, V, K, T, loss, lse, row_kl, ws, nullptr,
+                     nullptr, s, LossExt(), reinterpret_cast<float*>(ws + kp.off_z));
+}
+
+kd_status kd_topk_kl_backward_keep_logits(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,
+                                          const float* topk_logit, const float* lse, const float* grad_loss,
+                                          int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                                          uint16_t* dH, float* dW, void* workspace, size_t workspace_bytes,
+                                          void* hip_stream) {
+  kd::KeepLogitsPlan kp;
+  const kd_status st = kd::make_keep_logits_plan(N, D, V, K, T, chunk, &kp);
+  if (st != KD_OK) return st;
+  if (bad_ptr(dW, 16)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (bad_ptr(H, 16) || bad_ptr(W, 16) || bad_ptr(topk_idx, 4) || bad_ptr(topk_logit, 4) ||
+                bad_ptr(lse, 4) || bad_ptr(dH, 16)))
+    return KD_ERR_INVALID_ARG;
+  if (grad_loss != nullptr && !kd::aligned(grad_loss, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (workspace == nullptr || workspace_bytes < kp.bytes)) return KD_ERR_WORKSPACE;
+  if (workspace != nullptr && !kd::aligned(workspace, 256)) return KD_ERR_INVALID_ARG;
+  if (N == 0) return KD_OK;
+  char* ws = static_cast<char*>(workspace);
+  return run_backward(kp.base, H, W, topk_idx, topk_logit, nullptr, 0, lse, nullptr, grad_loss, N, D, V, K, T,
+                      dH, dW, ws, static_cast<hipStream_t>(hip_stream), LossExt(),
+                      reinterpret_cast<float*>(ws + kp.off_z));
 }
 
 kd_status kd_topk_kl_backward(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,

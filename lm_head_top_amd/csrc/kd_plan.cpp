@@ -142,6 +142,18 @@ kd_status make_keep_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, in
   return KD_OK;
 }
 
+kd_status make_keep_logits_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                                KeepLogitsPlan* plan) {
+  if (plan == nullptr) return KD_ERR_INVALID_ARG;
+  KeepLogitsPlan kp;
+  const kd_status st = make_plan(N, D, V, K, T, chunk, &kp.base);
+  if (st != KD_OK) return st;
+  kp.off_z = align_up(kp.base.bytes);
+  kp.bytes = align_up(kp.off_z + size_t(N > 0 ? N : 1) * size_t(kp.base.Vp) * 4);
+  *plan = kp;
+  return KD_OK;
+}
+
 kd_status make_dense_plan(int64_t N, int64_t D, int64_t V, float T, int64_t chunk, DensePlan* plan) {
   if (plan == nullptr) return KD_ERR_INVALID_ARG;
   if (V % 4 != 0) return KD_ERR_INVALID_ARG;  // the teacher is read 4 logits at a time

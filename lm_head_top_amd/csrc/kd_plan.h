@@ -57,6 +57,17 @@ struct KeepPlan {
 kd_status make_keep_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
                          KeepPlan* plan);
 
+// Kept-logits mode (the comparator that keeps every chunk's fp32 logits from
+// the forward for the backward, which then skips the recompute GEMM): the
+// plan of the top-K path plus z for all N positions, fp32 [N, Vp].
+struct KeepLogitsPlan {
+  Plan base;
+  size_t off_z = 0, bytes = 0;
+};
+
+kd_status make_keep_logits_plan(int64_t N, int64_t D, int64_t V, int32_t K, float T, int64_t chunk,
+                                KeepLogitsPlan* plan);
+
 // Dense-teacher mode (full-vocabulary teacher logits streamed per chunk
 // instead of a top-K cache): the plan of the top-K path with K = 1 (its cache
 // buffers go unused) plus the teacher's per-tile partials.

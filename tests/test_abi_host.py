@@ -84,6 +84,34 @@ def test_workspace_size_rejects(lib):
     assert f(0, 16, 100, 5, 4) > 0            # empty batch is valid
 
 
+def test_keep_logits_workspace_adds_one_fp32_grid(lib):
+    base = kd.workspace_size(8192, 4096, 131072, 100, 1024)
+    kept = kd.keep_logits_workspace_size(8192, 4096, 131072, 100, 1024)
+    assert 0 <= kept - base - 8192 * 131072 * 4 <= 512
+    # V = 201088 keeps rows of Vp = 201216 (V rounded up to 256)
+    b2 = kd.workspace_size(1000, 64, 201088, 8, 256)
+    k2 = kd.keep_logits_workspace_size(1000, 64, 201088, 8, 256)
+    assert 0 <= k2 - b2 - 1000 * 201216 * 4 <= 512
+    assert kd.keep_logits_workspace_size(10, 12, 100, 5, 4) == 0   # D not a multiple of 8
+
+
+def test_keep_logits_entry_points_reject(lib):
+    v = ctypes.c_void_p
+    ok = 1 << 24
+    f = lib.kd_topk_kl_forward_keep_logits
+    assert f(v(ok), v(ok), v(ok), v(ok), 4, 16, 64, 3, 1.0, 2, v(0), v(ok), v(0), v(ok), 1 << 30,
+             v(0)) == KD_ERR_INVALID_ARG                                     # no loss
+    assert f(v(ok), v(ok), v(ok), v(ok), 4, 16, 64, 3, 1.0, 2, v(ok), v(ok), v(0), v(ok), 16,
+             v(0)) == KD_ERR_WORKSPACE
+    b = lib.kd_topk_kl_backward_keep_logits
+    assert b(v(ok), v(ok), v(ok), v(ok), v(ok), v(0), 4, 16, 64, 3, 1.0, 2, v(ok), v(0), v(ok), 1 << 30,
+             v(0)) == KD_ERR_INVALID_ARG                                     # no dW
+    assert b(v(ok), v(ok), v(ok), v(ok), v(ok), v(0), 4, 16, 64, 3, 1.0, 2, v(ok), v(ok), v(ok), 16,
+             v(0)) == KD_ERR_WORKSPACE
+    assert b(v(ok), v(ok), v(ok), v(ok), v(ok), v(0), 4, 16, 64, 3, 0.0, 2, v(ok), v(ok), v(ok), 1 << 30,
+             v(0)) == KD_ERR_INVALID_ARG                                     # T = 0
+
+
 def test_workspace_size_limits_of_32bit_operand_offsets(lib):
     f = kd.workspace_size
     # a chunk whose G rows exceed 2^31 elements is accepted (its gradient GEMMs
