@@ -4,16 +4,21 @@
 // changes"; "The $250GB Memory Spike That Killed Distillation Projects Is Now
 // Optional", section "Offline Top-K").
 //
-// One workgroup per row, one pass over the row in HBM.  Every logit becomes a
-// 64-bit key (order-preserving bits of the logit, then the complement of the
-// id), so "larger key" is exactly "larger logit, or equal logit and lower id"
-// and all keys of a row are distinct.  Keys above the running threshold (the
-// K-th best key kept so far) are appended to an LDS candidate list; when the
-// list holds TRIG keys (and at least K) it is sorted (bitonic, in LDS), cut to
-// the K best and the threshold raised.  For random logits a row of 131072 admits a
-// few thousand candidates, so the row is read once and sorted about three
-// times.  The next batch of the row is loaded into registers while the
-// current one is filtered.
+// One wave per row, one pass over the row in HBM, no workgroup barriers.
+// Every logit becomes a 64-bit key (order-preserving bits of the logit, then
+// the complement of the id), so "larger key" is exactly "larger logit, or
+// equal logit and lower id" and all keys of a row are distinct.  The row
+// streams in batches of 1024 logits (16-byte loads, 1 KiB per load
+// instruction), two batches in flight while a third is filtered, so the
+// wave keeps 8 KiB of loads outstanding.  A batch is first tested as floats:
+// the max of each lane's values against the float floor of the threshold
+// (the K-th best key kept so far), one wave-wide test per batch.  Only when
+// some lane passes are the 64-bit keys formed and those above the threshold
+// appended to the wave's candidate list in LDS.  When the list reaches TRIG
+// keys it is cut to the K best: a 64-step bitwise search finds the K-th
+// largest key (counting with ballots), the keys at or above it are packed to
+// the front, and it becomes the threshold.  At the end the K survivors are
+// sorted in registers (bitonic, across the wave's lanes).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,23 +29,13 @@
 namespace kd {
 namespace {
 
-#ifndef KD_TOPK_THREADS
-#define KD_TOPK_THREADS 256
-#endif
-#ifndef KD_TOPK_BATCH
-#define KD_TOPK_BATCH 2048
-#endif
-#ifndef KD_TOPK_TRIG
-#define KD_TOPK_TRIG 512
-#endif
-constexpr int TS = KD_TOPK_THREADS;      // threads per row
-constexpr int PER_IT = KD_TOPK_BATCH;    // logits per batch
-constexpr int CAP = 2 * PER_IT;          // candidate keys in LDS (32 KiB at 2048: 4 rows per CU)
-// The list is compacted (and the threshold raised) once it holds TRIG keys,
-// so the threshold follows the running K-th best closely; at most CAP - PER_IT.
-constexpr int TRIG = KD_TOPK_TRIG < CAP - PER_IT ? KD_TOPK_TRIG : CAP - PER_IT;
-static_assert(CAP >= 2 * PER_IT && CAP - PER_IT >= 256, "a batch must fit beside a full list");
-static_assert(PER_IT % (TS * 8) == 0, "a batch is whole 16-byte loads of bf16 for every thread");
+constexpr int TW = 4;            // rows (waves) per workgroup
+constexpr int EB = 1024;         // logits per batch per wave
+constexpr int CAPW = 1280;       // candidate keys per wave in LDS (4 waves: 40 KiB per workgroup)
+constexpr int TRIG = CAPW - EB;  // the list is cut once it holds this many keys
+constexpr int KPL = CAPW / 64;   // list keys per lane when the list is cut
+static_assert(TRIG >= KD_MAX_K, "a cut list keeps K keys below the trigger");
+static_assert(KD_MAX_K <= 256, "the final sort holds 4 keys per lane");
 
 // Order-preserving 32-bit image of a float with -0.0 taken as +0.0.
 __device__ __forceinline__ uint32_t sortable(float x) {
@@ -66,168 +61,201 @@ __device__ __forceinline__ float key_floor(uint64_t thr) {
   return hi <= sortable(-INFINITY) ? -INFINITY : unsortable(hi);
 }
 
-// Appends the keys above thr (one wave-aggregated LDS atomic per wave).
-__device__ __forceinline__ void append(uint64_t key, bool valid, uint64_t thr, uint64_t* cand, int* cnt,
-                                       int lane) {
-  const bool take = valid && key > thr;
-  const uint64_t m = __ballot(take);
-  if (m == 0) return;
-  int base = 0;
-  if (lane == 0) base = atomicAdd(cnt, __popcll(m));
-  base = __shfl(base, 0);
-  if (take) cand[base + __popcll(m & ((uint64_t(1) << lane) - 1))] = key;
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Sorts cand[0, n) descending (pads to a power of two with key 0, which is
-// below every real key), leaves the K best at the front and returns the new
-// list length min(n, K).  All threads call it.  Each bitonic stage first loads
-// every pair a thread owns, then compares and stores, so a stage costs one LDS
-// round trip rather than one per pair (the pairs of a stage are disjoint).
-__device__ int compact(uint64_t* cand, int n, int K) {
-  int P = 2;
-  while (P < n) P <<= 1;
-  for (int i = n + threadIdx.x; i < P; i += TS) cand[i] = 0;
-  __syncthreads();
-  constexpr int MAXU = CAP / 2 / TS;  // pairs per thread at P = CAP
-  const int npairs = P >> 1;
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int lj = __builtin_ctz(j);
-      uint64_t a[MAXU], b[MAXU];
-      int ia[MAXU];
+// Orders this wave's LDS accesses for the compiler: LDS serves one wave's
+// instructions in issue order, so the wave sees its own earlier writes.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Cuts the wave's list cand[0, n) (n > K) to its K largest keys, packed at
+// the front; returns the K-th largest key T, found bit by bit from the top
+// as the largest value with at least K keys at or above it (each step counts
+// with one ballot per 64-key slot; branch-free over all slots, which measured
+// faster than limiting the scan to the slots in use or searching the value
+// and id words separately).
+__device__ uint64_t cut_list(uint64_t* cand, int n, int K, int lane) {
+  uint64_t key[KPL];
 #pragma unroll
-      for (int u = 0; u < MAXU; ++u) {
-        const int p = threadIdx.x + u * TS;
-        // pair p: i has bit lj clear, its partner sets it
-        const int i = ((p >> lj) << (lj + 1)) | (p & (j - 1));
-        ia[u] = i;
-        if (p < npairs) {
-          a[u] = cand[i];
-          b[u] = cand[i | j];
-        }
-      }
+  for (int j = 0; j < KPL; ++j) {
+    const int i = j * 64 + lane;
+    key[j] = i < n ? cand[i] : 0ull;  // key 0 lies below every real key
+  }
+  // keys are distinct, so that largest value is itself a key
+  uint64_t T = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t c = T | (1ull << bit);
+    int cnt = 0;
 #pragma unroll
-      for (int u = 0; u < MAXU; ++u) {
-        const int p = threadIdx.x + u * TS;
-        if (p < npairs) {
-          const int i = ia[u];
-          const bool desc = (i & k) == 0;
-          if (desc ? (a[u] < b[u]) : (a[u] > b[u])) {
-            cand[i] = b[u];
-            cand[i | j] = a[u];
-          }
-        }
-      }
-      __syncthreads();
+    for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(key[j] >= c));
+    if (cnt >= K) T = c;
+  }
+  wave_lds_fence();
+  int pos = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const bool keep = key[j] >= T && key[j] != 0ull;
+    const uint64_t m = __ballot(keep);
+    if (keep) cand[pos + __popcll(m & lanes_below(lane))] = key[j];
+    pos += __popcll(m);
+  }
+  wave_lds_fence();
+  return T;
+}
+
+// Compare-exchange of bitonic stage (k, j) for the 4 keys of this lane
+// (element i = 4 lane + r): the pair (i, i ^ j), larger first where i & k is 0.
+__device__ __forceinline__ void bitonic_step(uint64_t (&v)[4], int lane, int k, int j) {
+  if (j >= 4) {
+    const int lj = j >> 2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t lo = __shfl_xor(uint32_t(v[r]), lj);
+      const uint32_t hi = __shfl_xor(uint32_t(v[r] >> 32), lj);
+      const uint64_t o = (uint64_t(hi) << 32) | lo;
+      const int i = 4 * lane + r;
+      const bool lower = (i & j) == 0;  // the lower element of its pair
+      const bool desc = (i & k) == 0;
+      const bool keep_max = lower == desc;
+      v[r] = keep_max ? (v[r] > o ? v[r] : o) : (v[r] < o ? v[r] : o);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if ((r & j) != 0) continue;
+      const int i = 4 * lane + r;
+      const bool desc = (i & k) == 0;
+      const uint64_t a = v[r], b = v[r | j];
+      const bool swap = desc ? (a < b) : (a > b);
+      v[r] = swap ? b : a;
+      v[r | j] = swap ? a : b;
     }
   }
-  return n < K ? n : K;
 }
 
 // DT 0: fp32 logits, DT 1: bf16 logits.  VEC: 16-byte loads (the row length is
 // a multiple of 16 bytes and the base 16-byte aligned), else 2- or 4-byte loads.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(TS) void topk_select_kernel(const void* __restrict__ logits, int64_t V, int K,
-                                                         int32_t* __restrict__ out_idx,
-                                                         float* __restrict__ out_val) {
-  __shared__ uint64_t cand[CAP];
-  __shared__ int cnt;
-  const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
+__global__ __launch_bounds__(TW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void topk_select_kernel(const void* __restrict__ logits, int64_t N, int64_t V, int K,
+                        int32_t* __restrict__ out_idx, float* __restrict__ out_val) {
+  __shared__ uint64_t cand_all[TW * CAPW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = int64_t(blockIdx.x) * TW + wave;
+  if (row >= N) return;  // the whole wave; nothing below synchronises the workgroup
+  uint64_t* cand = cand_all + wave * CAPW;
   constexpr int ESZ = DT == 0 ? 4 : 2;
-  constexpr int EPL = 16 / ESZ;                   // elements per 16-byte load
-  constexpr int NL = VEC ? PER_IT / (TS * EPL) : PER_IT / TS;  // loads per thread per batch
-  const char* base = static_cast<const char*>(logits) + row * V * ESZ;
-  if (tid == 0) cnt = 0;
-  uint64_t thr = 0;
-  int n = 0;  // list length, the same in every thread after each barrier
-
-  // One batch: NL loads of 16 bytes (VEC) or of one element per thread.
+  constexpr int EPL = VEC ? 16 / ESZ : 1;  // logits per load
+  constexpr int U = EB / (64 * EPL);        // loads per lane per batch
   using Reg = typename std::conditional<VEC, uint4, uint32_t>::type;
-  auto load = [&](int64_t e0, Reg (&r)[NL]) {
+  const char* base = static_cast<const char*>(logits) + row * V * ESZ;
+
+  // logit index of load u, element q of this lane in the batch at e0
+  auto elem_index = [&](int64_t e0, int u, int q) -> int64_t { return e0 + int64_t(u * 64 + lane) * EPL + q; };
+  auto load = [&](int64_t e0, Reg (&r)[U]) {
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = elem_index(e0, u, 0);
       if constexpr (VEC) {
-        const int64_t e = e0 + int64_t(u * TS + tid) * EPL;
         r[u] = e < V ? *reinterpret_cast<const uint4*>(base + e * ESZ) : make_uint4(0, 0, 0, 0);
       } else {
-        const int64_t e = e0 + u * TS + tid;
         r[u] = e >= V ? 0u
                       : (DT == 0 ? reinterpret_cast<const uint32_t*>(base)[e]
                                  : uint32_t(reinterpret_cast<const uint16_t*>(base)[e]));
       }
     }
   };
-  // Most logits cannot beat the threshold: each is first compared as a float
-  // against key_floor(thr) (a superset of the exact test), one ballot drops a
-  // batch for the whole wave, and the 64-bit key, the exact test and the
-  // append run only for slots where some lane passes.
-  float thr_f = -INFINITY;
-  auto filter = [&](int64_t e0, const Reg (&r)[NL]) {
-    bool any = false;
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      if constexpr (VEC) {
-        const int64_t e = e0 + int64_t(u * TS + tid) * EPL;  // the row holds whole 16-byte chunks
-        const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) {
-          const float x = DT == 0 ? __uint_as_float(w[q]) : bf16_to_f32((w[q / 2] >> (16 * (q & 1))) & 0xffffu);
-          any |= e < V && x >= thr_f;
-        }
-      } else {
-        const int64_t e = e0 + u * TS + tid;
-        const float x = DT == 0 ? __uint_as_float(r[u]) : bf16_to_f32(r[u]);
-        any |= e < V && x >= thr_f;
-      }
-    }
-    if (__ballot(any) == 0) return;
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      if constexpr (VEC) {
-        const int64_t e = e0 + int64_t(u * TS + tid) * EPL;
-        const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) {
-          const float x = DT == 0 ? __uint_as_float(w[q]) : bf16_to_f32((w[q / 2] >> (16 * (q & 1))) & 0xffffu);
-          const bool pass = e < V && x >= thr_f;
-          if (__ballot(pass) == 0) continue;
-          append(make_key(x, uint32_t(e + q)), pass, thr, cand, &cnt, lane);
-        }
-      } else {
-        const int64_t e = e0 + u * TS + tid;
-        const float x = DT == 0 ? __uint_as_float(r[u]) : bf16_to_f32(r[u]);
-        const bool pass = e < V && x >= thr_f;
-        if (__ballot(pass) == 0) continue;
-        append(make_key(x, uint32_t(e)), pass, thr, cand, &cnt, lane);
-      }
+  auto value = [&](const Reg (&r)[U], int u, int q) -> float {
+    if constexpr (VEC) {
+      const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+      return DT == 0 ? __uint_as_float(w[q]) : bf16_to_f32((w[q / 2] >> (16 * (q & 1))) & 0xffffu);
+    } else {
+      return DT == 0 ? __uint_as_float(r[u]) : bf16_to_f32(r[u]);
     }
   };
 
-  __syncthreads();
-  Reg nxt[NL], cur[NL];
-  load(0, nxt);
-  for (int64_t e0 = 0; e0 < V; e0 += PER_IT) {
+  uint64_t thr = 0;  // keys above thr may enter the list
+  float thr_f = -INFINITY;
+  int n = 0;  // keys in the list (the same in every lane)
+  auto filter = [&](int64_t e0, const Reg (&r)[U]) {
+    if (e0 >= V) return;
+    float m = -INFINITY;
+    if (e0 + EB <= V) {  // a whole batch (uniform): no per-logit bounds test
 #pragma unroll
-    for (int u = 0; u < NL; ++u) cur[u] = nxt[u];
-    if (e0 + PER_IT < V) load(e0 + PER_IT, nxt);  // the next batch is in flight during the filter
-    filter(e0, cur);
-    __syncthreads();
-    n = cnt;
-    __syncthreads();  // every thread has the same n before any thread appends again
-    if (n >= TRIG && n >= K) {
-      n = compact(cand, n, K);
-      thr = cand[K - 1];  // n >= K keys were admitted, so n == K now
-      thr_f = key_floor(thr);
-      if (tid == 0) cnt = n;
-      __syncthreads();
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) m = fmaxf(m, value(r, u, q));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) {
+          const float x = value(r, u, q);
+          m = elem_index(e0, u, q) < V ? fmaxf(m, x) : m;
+        }
     }
+    if (__ballot(m >= thr_f) == 0) return;  // nothing in this batch can enter
+    wave_lds_fence();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const float x = value(r, u, q);
+        const int64_t e = elem_index(e0, u, q);
+        const bool pass = e < V && x >= thr_f;
+        if (__ballot(pass) == 0) continue;
+        const uint64_t key = make_key(x, uint32_t(e));
+        const bool take = pass && key > thr;
+        const uint64_t mk = __ballot(take);
+        if (take) cand[n + __popcll(mk & lanes_below(lane))] = key;
+        n += __popcll(mk);
+      }
+    wave_lds_fence();
+    if (n >= TRIG && n > K) {
+      thr = cut_list(cand, n, K, lane);
+      thr_f = key_floor(thr);
+      n = K;
+    }
+  };
+
+  // three register sets: two batches in flight while the third is filtered
+  // (a fourth set measured no faster)
+  Reg ra[U], rb[U], rc[U];
+  load(0, ra);
+  load(EB, rb);
+  load(2 * EB, rc);
+  for (int64_t e0 = 0; e0 < V; e0 += 3 * EB) {
+    filter(e0, ra);
+    load(e0 + 3 * EB, ra);
+    filter(e0 + EB, rb);
+    load(e0 + 4 * EB, rb);
+    filter(e0 + 2 * EB, rc);
+    load(e0 + 5 * EB, rc);
   }
-  n = compact(cand, n, K);
-  for (int i = tid; i < n; i += TS) {
-    const uint64_t key = cand[i];
-    out_idx[row * K + i] = int32_t(~uint32_t(key));
-    out_val[row * K + i] = unsortable(uint32_t(key >> 32));
+  if (n > K) {
+    cut_list(cand, n, K, lane);
+    n = K;
+  }
+  // sort the n <= K <= 256 survivors (padded with key 0) largest first
+  uint64_t v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * lane + r;
+    v[r] = i < n ? cand[i] : 0ull;
+  }
+  for (int k = 2; k <= 256; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) bitonic_step(v, lane, k, j);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * lane + r;
+    if (i < n) {
+      out_idx[row * K + i] = int32_t(~uint32_t(v[r]));
+      out_val[row * K + i] = unsortable(uint32_t(v[r] >> 32));
+    }
   }
 }
 
@@ -235,17 +263,17 @@ __global__ __launch_bounds__(TS) void topk_select_kernel(const void* __restrict_
 
 hipError_t launch_topk_select(const void* logits, int dtype, bool vec, int64_t N, int64_t V, int K,
                               int32_t* idx, float* val, hipStream_t s) {
-  const dim3 grid{unsigned(N), 1, 1}, block{unsigned(TS), 1, 1};
+  const dim3 grid{unsigned((N + TW - 1) / TW), 1, 1}, block{unsigned(TW * 64), 1, 1};
   if (dtype == 0) {
     if (vec)
-      hipLaunchKernelGGL((topk_select_kernel<0, true>), grid, block, 0, s, logits, V, K, idx, val);
+      hipLaunchKernelGGL((topk_select_kernel<0, true>), grid, block, 0, s, logits, N, V, K, idx, val);
     else
-      hipLaunchKernelGGL((topk_select_kernel<0, false>), grid, block, 0, s, logits, V, K, idx, val);
+      hipLaunchKernelGGL((topk_select_kernel<0, false>), grid, block, 0, s, logits, N, V, K, idx, val);
   } else {
     if (vec)
-      hipLaunchKernelGGL((topk_select_kernel<1, true>), grid, block, 0, s, logits, V, K, idx, val);
+      hipLaunchKernelGGL((topk_select_kernel<1, true>), grid, block, 0, s, logits, N, V, K, idx, val);
     else
-      hipLaunchKernelGGL((topk_select_kernel<1, false>), grid, block, 0, s, logits, V, K, idx, val);
+      hipLaunchKernelGGL((topk_select_kernel<1, false>), grid, block, 0, s, logits, N, V, K, idx, val);
   }
   return hipGetLastError();
 }
