@@ -78,6 +78,11 @@
 #ifndef KD_DW_BAND
 #define KD_DW_BAND 4
 #endif
+// logits tile order: 0 = position tile fastest within a vocab tile; b > 0 =
+// bands of b position tiles, position tile fastest within a band
+#ifndef KD_LOGITS_BAND
+#define KD_LOGITS_BAND 4
+#endif
 // dH tile order: bands of this many row tiles, row tile fastest
 #ifndef KD_DH_BAND
 #define KD_DH_BAND 4
@@ -773,7 +778,17 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   const int total = a.nvt * a.npt;
   const int tile = xcd_remap(blockIdx.x, total);
+#if KD_LOGITS_BAND > 0
+  // bands of up to KD_LOGITS_BAND position tiles, position tile fastest: the
+  // 32 tiles an XCD runs at once cover 32 / band vocab tiles x band position
+  // tiles, whose operand strips its L2 shares
+  constexpr int LB = KD_LOGITS_BAND;
+  const int band = tile / (LB * a.nvt), bw = min(LB, a.npt - LB * band);
+  const int bi = tile - band * LB * a.nvt;
+  const int pt = LB * band + bi % bw, vt = bi / bw;
+#else
   const int vt = tile / a.npt, pt = tile - vt * a.npt;
+#endif
   const int v0 = vt * kTile, p0 = pt * kTile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -1145,12 +1160,13 @@ __global__ __launch_bounds__(NT) void dense_combine_kernel(DenseCombineArgs a) {
 // loss = sum_n w_n l_n / sum_n w_n (w_n = 1 without weights; 0 for an empty
 // or all-zero weight), summed in fp64 in a fixed order.  Also leaves
 // 1 / sum_n w_n in *inv_wsum when asked (the backward's per-row factor).
-__global__ __launch_bounds__(NT) void finalize_kernel(const float* __restrict__ rowl, const float* __restrict__ w,
+constexpr int FT = 1024;  // threads of the finalize kernel
+__global__ __launch_bounds__(FT) void finalize_kernel(const float* __restrict__ rowl, const float* __restrict__ w,
                                                       int64_t N, float* __restrict__ loss, float* inv_wsum) {
-  __shared__ double red[NT], redw[NT];
+  __shared__ double red[FT], redw[FT];
   const int tid = threadIdx.x;
   double acc = 0.0, aw = 0.0;
-  for (int64_t i = tid; i < N; i += NT) {
+  for (int64_t i = tid; i < N; i += FT) {
     const double wi = w != nullptr ? double(w[i]) : 1.0;
     if (rowl != nullptr && wi != 0.0) acc += wi * double(rowl[i]);
     aw += wi;
@@ -1158,7 +1174,7 @@ __global__ __launch_bounds__(NT) void finalize_kernel(const float* __restrict__ 
   red[tid] = acc;
   redw[tid] = aw;
   __syncthreads();
-  for (int o = NT / 2; o > 0; o >>= 1) {
+  for (int o = FT / 2; o > 0; o >>= 1) {
     if (tid < o) {
       red[tid] += red[tid + o];
       redw[tid] += redw[tid + o];
@@ -1422,7 +1438,7 @@ hipError_t launch_dense_combine(const DenseCombineArgs& a, hipStream_t s) {
 
 hipError_t launch_finalize(const float* rowl, const float* w, int64_t N, float* loss, float* inv_wsum,
                            hipStream_t s) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(NT), 0, s, rowl, w, N, loss, inv_wsum);
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(FT), 0, s, rowl, w, N, loss, inv_wsum);
   return hipGetLastError();
 }
 
