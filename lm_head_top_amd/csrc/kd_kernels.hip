@@ -38,6 +38,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kd_kernels.h"
 
 // Build knobs (defaults are the measured best on MI355X)
@@ -77,6 +79,11 @@
 // tile fastest within a band
 #ifndef KD_DW_BAND
 #define KD_DW_BAND 4
+#endif
+// logits kernels: 0 = one workgroup per tile; 1 = one workgroup per compute
+// unit looping over tiles
+#ifndef KD_PERSIST_LOGITS
+#define KD_PERSIST_LOGITS 1
 #endif
 // logits tile order: 0 = position tile fastest within a vocab tile; b > 0 =
 // bands of b position tiles, position tile fastest within a band
@@ -774,10 +781,9 @@ __device__ __forceinline__ void teacher_column(const void* t, int dtype, int64_t
 // 0: forward epilogue, 1: backward epilogue, 2: forward epilogue that also
 // stores z, 3: dense-teacher forward epilogue, 4: dense-teacher backward epilogue
 template <int MODE>
-KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+__device__ __forceinline__ void logits_tile(const LogitsArgs& a, int t, char* smem) {
   const int total = a.nvt * a.npt;
-  const int tile = xcd_remap(blockIdx.x, total);
+  const int tile = xcd_remap(t, total);
 #if KD_LOGITS_BAND > 0
   // bands of up to KD_LOGITS_BAND position tiles, position tile fastest: the
   // 32 tiles an XCD runs at once cover 32 / band vocab tiles x band position
@@ -1050,6 +1056,23 @@ KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
       __syncthreads();
     }
   }
+}
+
+template <int MODE>
+KD_GEMM_KERNEL void logits_kernel(LogitsArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+#if KD_PERSIST_LOGITS
+  // one workgroup per compute unit walks the tiles b, b + grid, ...: the
+  // tiles an XCD runs at a time stay those of the one-tile-per-workgroup grid
+  // (the grid is a multiple of 8), without a workgroup launch between them
+  const int total = a.nvt * a.npt;
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    logits_tile<MODE>(a, t, smem);
+    __syncthreads();  // the next tile's loads refill the LDS this epilogue read
+  }
+#else
+  logits_tile<MODE>(a, blockIdx.x, smem);
+#endif
 }
 
 // ----------------------------------------------------------------- combine ---
@@ -1392,13 +1415,32 @@ hipError_t launch_bucket(const BucketArgs& a, int npt, int nchunks, hipStream_t 
   return hipGetLastError();
 }
 
+// Workgroups of a logits launch: one per tile, or with KD_PERSIST_LOGITS one
+// per compute unit of the current device (a multiple of 8), at most one per tile.
+unsigned logits_grid(const LogitsArgs& a) {
+  const unsigned tiles = unsigned(a.nvt) * unsigned(a.npt);
+  if (!KD_PERSIST_LOGITS) return tiles;
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return tiles;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return tiles;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  const unsigned g = unsigned(n) / 8 * 8;
+  return g == 0 || tiles <= g ? tiles : g;
+}
+
 hipError_t launch_logits_fwd(const LogitsArgs& a, hipStream_t s) {
+  const dim3 grid(logits_grid(a));
   if (a.tlog != nullptr)
-    hipLaunchKernelGGL(logits_kernel<3>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+    hipLaunchKernelGGL(logits_kernel<3>, grid, dim3(GT), 0, s, a);
   else if (a.zkeep != nullptr)
-    hipLaunchKernelGGL(logits_kernel<2>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+    hipLaunchKernelGGL(logits_kernel<2>, grid, dim3(GT), 0, s, a);
   else
-    hipLaunchKernelGGL(logits_kernel<0>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+    hipLaunchKernelGGL(logits_kernel<0>, grid, dim3(GT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1419,10 +1461,11 @@ hipError_t launch_keep_grad(float* z, const float* lse, const int32_t* idx, cons
 }
 
 hipError_t launch_logits_bwd(const LogitsArgs& a, hipStream_t s) {
+  const dim3 grid(logits_grid(a));
   if (a.tlog != nullptr)
-    hipLaunchKernelGGL(logits_kernel<4>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+    hipLaunchKernelGGL(logits_kernel<4>, grid, dim3(GT), 0, s, a);
   else
-    hipLaunchKernelGGL(logits_kernel<1>, dim3(a.nvt * a.npt), dim3(GT), 0, s, a);
+    hipLaunchKernelGGL(logits_kernel<1>, grid, dim3(GT), 0, s, a);
   return hipGetLastError();
 }
 
