@@ -53,6 +53,19 @@
  *     backward may share one workspace when issued in order on one stream.
  *   - Results are deterministic: the same inputs give bit-identical outputs
  *     (rows with duplicate ids excepted).
+ *
+ * Debug aids (off the hot path):
+ *   - KD_VALIDATE=1 in the environment (read at every call) makes each entry
+ *     point that reads the top-K cache check its ids first, on its stream,
+ *     and wait for the answer: an id outside [0, V) returns
+ *     KD_ERR_INVALID_IDS before any other work.  Such calls synchronise the
+ *     host with the stream and cannot be captured into a HIP graph.
+ *   - libkdtopk_debug.so, built beside libkdtopk.so with the same exports,
+ *     checks the indices of the cache-entry scatters and gathers on the
+ *     device (bucketing, the forward's gather, the backward's scatter)
+ *     against the extents they address.  A failed check skips that access;
+ *     the top-K forward and backward then wait for their stream at the end
+ *     and return KD_ERR_DEBUG_CHECK.  Arithmetic is that of libkdtopk.so.
  */
 #ifndef KDTOPK_H
 #define KDTOPK_H
@@ -72,7 +85,9 @@ typedef enum kd_status {
   KD_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad T */
   KD_ERR_UNSUPPORTED = 2, /* valid but outside this library's limits */
   KD_ERR_WORKSPACE = 3,   /* workspace smaller than kd_topk_kl_workspace_size */
-  KD_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+  KD_ERR_HIP = 4,         /* a HIP runtime call or launch failed */
+  KD_ERR_INVALID_IDS = 5, /* KD_VALIDATE=1 only: a cached id lies outside [0, V) */
+  KD_ERR_DEBUG_CHECK = 6  /* debug library only: a device-side bounds check failed */
 } kd_status;
 
 /*

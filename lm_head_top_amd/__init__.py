@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = [
-    "lib_path", "load_library", "workspace_size", "forward", "forward_noalloc", "backward", "validate",
+    "lib_path", "debug_lib_path", "load_library", "swap_library", "workspace_size", "forward", "forward_noalloc", "backward", "validate",
     "KDTopKKL", "profile_enable", "profile_read", "KERNELS", "KDError", "topk_select",
     "keep_workspace_size", "forward_keep", "backward_keep",
     "keep_logits_workspace_size", "forward_keep_logits", "backward_keep_logits",
@@ -30,7 +30,8 @@ KERNELS = {
 }
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem size",
-           3: "workspace too small", 4: "HIP launch failed"}
+           3: "workspace too small", 4: "HIP launch failed", 5: "cached id outside [0, V)",
+           6: "device bounds check failed"}
 
 
 class KDError(RuntimeError):
@@ -45,12 +46,13 @@ def lib_path() -> str:
     return os.path.join(_HERE, _LIB_NAME)
 
 
-def load_library():
-    """Loads libkdtopk.so (built by ``python -m lm_head_top_amd.build``)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    path = lib_path()
+def debug_lib_path() -> str:
+    """libkdtopk_debug.so: the same exports, with device-side bounds checks on
+    the cache-entry scatters and gathers (built beside libkdtopk.so)."""
+    return os.path.join(_HERE, "libkdtopk_debug.so")
+
+
+def _open(path: str):
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build it with `python -m lm_head_top_amd.build` "
@@ -60,7 +62,28 @@ def load_library():
     # and streams torch hands over belong to the same runtime (loaded the other
     # way round, the process would hold two HIP runtimes).
     import torch  # noqa: F401
-    lib = ctypes.CDLL(path)
+    return _configure(ctypes.CDLL(path))
+
+
+def load_library():
+    """Loads libkdtopk.so (built by ``python -m lm_head_top_amd.build``)."""
+    global _lib
+    if _lib is None:
+        _lib = _open(lib_path())
+    return _lib
+
+
+def swap_library(lib):
+    """Points the entry points at another build of the library: a path (say
+    debug_lib_path()) or a handle an earlier call returned.  Returns the
+    handle in use before, so a caller can switch back."""
+    global _lib
+    prev = load_library()
+    _lib = _open(lib) if isinstance(lib, str) else lib
+    return prev
+
+
+def _configure(lib):
     c_i64, c_i32, c_f, c_vp, c_sz = (ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_size_t)
     lib.kd_topk_kl_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i64]
@@ -115,7 +138,6 @@ def load_library():
     lib.kd_profile_read.argtypes = [c_i32, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
     lib.kd_profile_read.restype = ctypes.c_int
-    _lib = lib
     return lib
 
 

@@ -17,6 +17,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libkdtopk.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# the same library with device-side bounds checks on the cache-entry
+# scatters and gathers (KD_DEBUG_BOUNDS), for debugging only
+DEBUG_LIB_NAME = "libkdtopk_debug.so"
+DEBUG_LIB_PATH = os.path.join(HERE, DEBUG_LIB_NAME)
 ARCH = "gfx950"
 
 HIP_SOURCES = ["kd_kernels.hip", "kd_topk_select.hip", "kd_capi.hip"]
@@ -49,27 +53,31 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compiles every source and links the shared library; returns its path."""
+    """Compiles every source and links the shared library and its debug
+    variant; returns the library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = _hipcc()
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
     jobs = []
-    objs = []
-    for src in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, src + ".o")
-        objs.append(obj)
-        jobs.append([hipcc, "-x", "hip", *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+    objs = {LIB_PATH: [], DEBUG_LIB_PATH: []}
+    for lib, defs, tag in ((LIB_PATH, [], ""), (DEBUG_LIB_PATH, ["-DKD_DEBUG_BOUNDS=1"], ".debug")):
+        for src in HIP_SOURCES:
+            obj = os.path.join(BUILD_DIR, src + tag + ".o")
+            objs[lib].append(obj)
+            jobs.append([hipcc, "-x", "hip", *HIP_FLAGS, *defs, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        objs.append(obj)
+        for lib in objs:
+            objs[lib].append(obj)
         jobs.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
                      os.path.join(CSRC, src), "-o", obj])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:
             f.result()
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
+    for lib, lobjs in objs.items():
+        tmp = lib + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *lobjs, "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB_PATH
 
 

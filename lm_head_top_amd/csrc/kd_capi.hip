@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -64,6 +65,34 @@ kd_status hip_failed(hipError_t e) {
 
 bool bad_ptr(const void* p, size_t align) { return p == nullptr || !kd::aligned(p, align); }
 
+// KD_VALIDATE=1 in the environment (read at every call): the top-K entry
+// points first check the cache's ids on their stream and wait for the answer.
+bool validate_requested() {
+  const char* v = std::getenv("KD_VALIDATE");
+  return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+// The ids check of KD_VALIDATE=1 (flags: a device int32 the call may use).
+kd_status validate_if_requested(const int32_t* topk_idx, int64_t N, int32_t K, int64_t V, int32_t* flags,
+                                hipStream_t s) {
+  if (topk_idx == nullptr || N == 0 || !validate_requested()) return KD_OK;
+  hipError_t e = kd::launch_validate(topk_idx, N, K, V, flags, s);
+  int32_t h = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, flags, sizeof h, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_failed(e);
+  return (h & 1) != 0 ? KD_ERR_INVALID_IDS : KD_OK;
+}
+
+// End of a top-K call: in debug builds, waits for the stream and reports a
+// failed device-side bounds check; otherwise KD_OK at once.
+kd_status debug_done(hipStream_t s) {
+  unsigned bits = 0;
+  const hipError_t e = kd::debug_fault_take(&bits, s);
+  if (e != hipSuccess) return hip_failed(e);
+  return bits != 0 ? KD_ERR_DEBUG_CHECK : KD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +114,10 @@ const char* kd_status_string(kd_status s) {
       return "workspace too small";
     case KD_ERR_HIP:
       return "HIP launch failed";
+    case KD_ERR_INVALID_IDS:
+      return "cached id outside [0, V)";
+    case KD_ERR_DEBUG_CHECK:
+      return "device bounds check failed";
   }
   return "unknown status";
 }
@@ -158,6 +191,11 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
   float* rowkl = row_kl != nullptr ? row_kl : reinterpret_cast<float*>(ws + p.off_rowkl);
   const float invT = 1.f / T;
   const float g_scale = float(1.0 / (double(N) * double(T)));
+  {
+    const kd_status vs =
+        validate_if_requested(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.off_scalar + 64), s);
+    if (vs != KD_OK) return vs;
+  }
 
   const int KE = K + (ext.labels != nullptr ? 1 : 0);
   int gj = 0;  // chunk within its group
@@ -219,7 +257,7 @@ kd_status run_forward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, c
                                      g_scale, gall + row0 * p.Vp, s));
   }
   KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(rowkl, ext.row_w, N, loss, nullptr, s));
-  return KD_OK;
+  return debug_done(s);
 }
 
 // The backward's chunk loop: recompute each chunk's logits and form G_c (top-K
@@ -244,6 +282,11 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
   const int ktiles = int(p.Vp / kd::gemm_bk());
   const int kps = (ktiles + p.grp_split - 1) / p.grp_split;
   const size_t esz = t_dtype == KD_DTYPE_F32 ? 4 : 2;
+  if (tlog == nullptr) {
+    const kd_status vs =
+        validate_if_requested(topk_idx, N, K, V, reinterpret_cast<int32_t*>(ws + p.off_scalar + 64), s);
+    if (vs != KD_OK) return vs;
+  }
   if (ext.row_w != nullptr)
     KD_LAUNCH(KD_KERNEL_FINALIZE, s, kd::launch_finalize(nullptr, ext.row_w, N, nullptr, inv_wsum, s));
   const int KE = K + (ext.labels != nullptr ? 1 : 0);
@@ -331,7 +374,7 @@ kd_status run_backward(const kd::Plan& p, const uint16_t* H, const uint16_t* W, 
       gj = 0;
     }
   }
-  return KD_OK;
+  return debug_done(s);
 }
 
 kd_status check_forward_ptrs(const uint16_t* H, const uint16_t* W, const int32_t* topk_idx,

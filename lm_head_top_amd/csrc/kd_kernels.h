@@ -141,6 +141,10 @@ hipError_t launch_keep_grad(float* z, const float* lse, const int32_t* idx, cons
 hipError_t launch_validate(const int32_t* idx, int64_t N, int K, int64_t V, int32_t* flags,
                            hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// Debug builds: waits for s, then returns (and clears) the bits of the
+// device-side bounds checks that failed since the last call.  Other builds
+// return 0 at once.
+hipError_t debug_fault_take(unsigned* bits, hipStream_t s);
 
 // Teacher top-K cache writer: one workgroup per row of logits [N, V] (dtype 0
 // fp32, 1 bf16; vec: 16-byte loads allowed).

@@ -94,6 +94,12 @@
 #ifndef KD_DH_BAND
 #define KD_DH_BAND 4
 #endif
+// Debug builds (1) check the indices of the cache-entry scatters and gathers
+// against the extents they address; a failed check skips the access and
+// sets a bit of a device word that the entry points read back.
+#ifndef KD_DEBUG_BOUNDS
+#define KD_DEBUG_BOUNDS 0
+#endif
 
 namespace kd {
 namespace {
@@ -125,6 +131,23 @@ constexpr int EPI_BYTES = (STAGE_FLOATS + 10 * kTile) * 4;
 constexpr int SMEM_BYTES =
     ring_bytes(KD_DEEP_LOGITS) > EPI_BYTES ? ring_bytes(KD_DEEP_LOGITS) : EPI_BYTES;
 constexpr uint32_t kOOB = 0xFFFFFFF0u;           // buffer offset past any operand: reads return 0
+
+#if KD_DEBUG_BOUNDS
+// bit 0: a bucketed entry's slot, bit 1: a forward gather, bit 2: a backward scatter
+__device__ unsigned debug_fault;
+#endif
+
+// True when ok; in debug builds a false check also records bit.
+__device__ __forceinline__ bool kd_check(bool ok, int bit) {
+#if KD_DEBUG_BOUNDS
+  if (!ok) atomicOr(&debug_fault, 1u << bit);
+  return ok;
+#else
+  (void)ok;
+  (void)bit;
+  return true;
+#endif
+}
 constexpr float LOG2E = 1.4426950408889634f;
 
 static_assert(BK == 32 || BK == 64, "BK");
@@ -710,7 +733,8 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
         const int rr = int((float(e) + 0.5f) * invK);
         const int k = e - rr * a.K;
         const int pos = atomicAdd(&cnt[((id[u] >> 8) << bsh) | sub], 1);
-        dst[pos] = (uint32_t(rr) << 17) | (uint32_t(id[u] & (kTile - 1)) << 9) | uint32_t(k);
+        if (kd_check(pos >= 0 && pos < nr * a.KE && rr < nr && k < a.K, 0))
+          dst[pos] = (uint32_t(rr) << 17) | (uint32_t(id[u] & (kTile - 1)) << 9) | uint32_t(k);
       }
   }
   if (labels != nullptr)
@@ -718,7 +742,8 @@ __global__ __launch_bounds__(BT) void bucket_kernel(BucketArgs a) {
       const int y = labels[r0 + rr];
       if (unsigned(y) < unsigned(a.V)) {
         const int pos = atomicAdd(&cnt[((y >> 8) << bsh) | sub], 1);
-        dst[pos] = (uint32_t(rr) << 17) | (uint32_t(y & (kTile - 1)) << 9) | uint32_t(a.K);
+        if (kd_check(pos >= 0 && pos < nr * a.KE && a.K < a.KE, 0))
+          dst[pos] = (uint32_t(rr) << 17) | (uint32_t(y & (kTile - 1)) << 9) | uint32_t(a.K);
       }
     }
   if (in_lds) {
@@ -947,6 +972,7 @@ __device__ __forceinline__ void logits_tile(const LogitsArgs& a, int t, char* sm
       }
     }
     if (MODE == 3 || ebeg == eend) return;
+    if (!kd_check(0 <= ebeg && ebeg <= eend && eend <= kTile * a.KE, 1)) return;
     // logits at the cached ids that fall in this tile
     for (int h = 0; h < 2; ++h) {
       stage_half(S, acc, wm, wn, lane, h);
@@ -957,7 +983,8 @@ __device__ __forceinline__ void logits_tile(const LogitsArgs& a, int t, char* sm
         if ((row >> 7) == h) {
           const int vl = int((pk >> 9) & 0xffu), k = int(pk & 0x1ffu);
           const float zv = S[(row & 127) * SLD + vl];
-          a.zsel[int64_t(p0 + row) * a.KE + k] = SCALED ? zv : zv * a.invT;
+          if (kd_check(k < a.KE && p0 + row < a.rows, 1))
+            a.zsel[int64_t(p0 + row) * a.KE + k] = SCALED ? zv : zv * a.invT;
         }
       }
       __syncthreads();
@@ -1018,17 +1045,19 @@ __device__ __forceinline__ void logits_tile(const LogitsArgs& a, int t, char* sm
         __builtin_amdgcn_sched_barrier(0);  // one column's loads in flight at a time
       }
     }
+    const bool ents_ok = !CACHE || kd_check(0 <= ebeg && ebeg <= eend && eend <= kTile * a.KE, 2);
     for (int h = 0; h < 2; ++h) {
       stage_half(S, acc, wm, wn, lane, h);
       __syncthreads();
       // minus alpha p at each cached id and beta at the label (scatter-add),
       // times gs w_n / sum w
-      for (int e = ebeg + tid; e < eend; e += GT) {
+      for (int e = ebeg + tid; ents_ok && e < eend; e += GT) {
         const uint32_t pk = ent[e];
         const int row = int(pk >> 17);
         if ((row >> 7) == h) {
           const int vl = int((pk >> 9) & 0xffu), k = int(pk & 0x1ffu);
           const int prow = p0 + row;
+          if (!kd_check(k < a.KE && prow < a.rows, 2)) continue;
           const float rs = a.row_w != nullptr ? a.row_w[prow] * iws : 1.f;
           const float mass = k < a.K ? a.alpha * a.p[int64_t(prow) * a.K + k] : a.beta;
           atomicAdd(S + (row & 127) * SLD + vl, -(gs * rs) * mass);
@@ -1514,6 +1543,22 @@ hipError_t launch_validate(const int32_t* idx, int64_t N, int K, int64_t V, int3
   hipLaunchKernelGGL(validate_kernel, dim3(unsigned(ceil_div(N, NT / 64))), dim3(NT), 0, s, idx, N, K, V,
                      flags);
   return hipGetLastError();
+}
+
+hipError_t debug_fault_take(unsigned* bits, hipStream_t s) {
+  *bits = 0;
+#if KD_DEBUG_BOUNDS
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(bits, HIP_SYMBOL(debug_fault), sizeof(unsigned));
+  if (e == hipSuccess && *bits != 0) {
+    const unsigned zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(debug_fault), &zero, sizeof(unsigned));
+  }
+  return e;
+#else
+  (void)s;
+  return hipSuccess;
+#endif
 }
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {

@@ -43,7 +43,31 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.kd_status_string(0) == b"ok"
     assert lib.kd_status_string(3) == b"workspace too small"
+    assert lib.kd_status_string(5) == b"cached id outside [0, V)"
+    assert lib.kd_status_string(6) == b"device bounds check failed"
     assert lib.kd_status_string(99) == b"unknown status"
+
+
+def test_debug_library_exports_the_same_symbols(lib):
+    path = kd.debug_lib_path()
+    if not os.path.exists(path):
+        pytest.skip("libkdtopk_debug.so not built")
+    dbg = ctypes.CDLL(path)
+    for name in _declared_functions():
+        assert hasattr(dbg, name), name
+    dbg.kd_topk_kl_workspace_size.restype = ctypes.c_size_t
+    args = (ctypes.c_int64(8192), ctypes.c_int64(4096), ctypes.c_int64(131072), ctypes.c_int32(100),
+            ctypes.c_int64(1024))
+    assert dbg.kd_topk_kl_workspace_size(*args) == lib.kd_topk_kl_workspace_size(8192, 4096, 131072, 100, 1024)
+
+
+def test_validate_env_does_not_touch_argument_checks(lib, monkeypatch):
+    # KD_VALIDATE=1 runs only after the host checks pass, so a rejected call
+    # still returns its status before any HIP call
+    monkeypatch.setenv("KD_VALIDATE", "1")
+    assert lib.kd_topk_kl_forward(None, None, None, None, 1, 8, 8, 1, 1.0, 1, None, None, None,
+                                  None, 0, None) == KD_ERR_INVALID_ARG
+    assert lib.kd_last_hip_error() == b""
 
 
 def test_last_hip_error_is_empty_without_a_failed_launch(lib):
