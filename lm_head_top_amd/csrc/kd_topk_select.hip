@@ -8,14 +8,14 @@
 // Every logit becomes a 64-bit key (order-preserving bits of the logit, then
 // the complement of the id), so "larger key" is exactly "larger logit, or
 // equal logit and lower id" and all keys of a row are distinct.  The row
-// streams in batches of 1024 logits (16-byte loads, 1 KiB per load
-// instruction), two batches in flight while a third is filtered, so the
-// wave keeps 8 KiB of loads outstanding.  A batch is first tested as floats:
-// the max of each lane's values against the float floor of the threshold
-// (the K-th best key kept so far), one wave-wide test per batch.  Only when
-// some lane passes are the 64-bit keys formed and those above the threshold
-// appended to the wave's candidate list in LDS.  When the list reaches TRIG
-// keys it is cut to the K best: a 64-step bitwise search finds the K-th
+// streams in batches of 1024 logits through a buffer descriptor (16-byte
+// loads, 1 KiB per load instruction, zeros past the row), two batches in
+// flight while a third is filtered.  Each load's values are first tested as
+// floats: their max against the float floor of the threshold (the K-th best
+// key kept so far), one wave-wide test per load.  Only when some lane passes
+// are the 64-bit keys formed and those above the threshold appended to the
+// wave's candidate list in LDS.  After every EI logits, a list of TRIG keys
+// or more is cut to the K best: a 64-step bitwise search finds the K-th
 // largest key (counting with ballots), the keys at or above it are packed to
 // the front, and it becomes the threshold.  At the end the K survivors are
 // sorted in registers (bitonic, across the wave's lanes).
@@ -29,12 +29,19 @@
 namespace kd {
 namespace {
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// logits that enter the candidate list between cut checks (at least one
+// load's worth): larger leaves more room below the cut trigger, so fewer
+// cuts per row
+#ifndef KD_TOPK_EI
+#define KD_TOPK_EI 512
+#endif
+
 constexpr int TW = 4;            // rows (waves) per workgroup
 constexpr int EB = 1024;         // logits per batch per wave
 constexpr int CAPW = 1280;       // candidate keys per wave in LDS (4 waves: 40 KiB per workgroup)
-constexpr int TRIG = CAPW - EB;  // the list is cut once it holds this many keys
 constexpr int KPL = CAPW / 64;   // list keys per lane when the list is cut
-static_assert(TRIG >= KD_MAX_K, "a cut list keeps K keys below the trigger");
 static_assert(KD_MAX_K <= 256, "the final sort holds 4 keys per lane");
 
 // Order-preserving 32-bit image of a float with -0.0 taken as +0.0.
@@ -144,26 +151,42 @@ __global__ __launch_bounds__(TW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void topk_select_kernel(const void* __restrict__ logits, int64_t N, int64_t V, int K,
                         int32_t* __restrict__ out_idx, float* __restrict__ out_val) {
   __shared__ uint64_t cand_all[TW * CAPW];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: say so, so the row's buffer descriptor sits in
+  // scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = int64_t(blockIdx.x) * TW + wave;
   if (row >= N) return;  // the whole wave; nothing below synchronises the workgroup
   uint64_t* cand = cand_all + wave * CAPW;
   constexpr int ESZ = DT == 0 ? 4 : 2;
   constexpr int EPL = VEC ? 16 / ESZ : 1;  // logits per load
-  constexpr int U = EB / (64 * EPL);        // loads per lane per batch
-  using Reg = typename std::conditional<VEC, uint4, uint32_t>::type;
+  constexpr int U = EB / (64 * EPL);  // loads per lane per batch
+  // logits that enter the list between cut checks (whole loads), and the
+  // list length that triggers a cut: a list below TRIG takes EI more keys
+  constexpr int EI = KD_TOPK_EI > 64 * EPL ? KD_TOPK_EI : 64 * EPL;
+  constexpr int UH = EI / (64 * EPL);
+  constexpr int TRIG = CAPW - EI;
+  static_assert(U % UH == 0 && TRIG >= KD_MAX_K, "cut checks at whole loads; a cut list fits below TRIG");
+  using Reg = typename std::conditional<VEC, u32x4, uint32_t>::type;
   const char* base = static_cast<const char*>(logits) + row * V * ESZ;
+  // VEC rows (under 2^31 bytes) load through a buffer descriptor: a load past
+  // the row returns zeros with no branch, so every batch issues the same
+  // loads and the loop keeps its two batches in flight
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, VEC ? int(V * ESZ) : 0, 0x00020000);
 
   // logit index of load u, element q of this lane in the batch at e0
-  auto elem_index = [&](int64_t e0, int u, int q) -> int64_t { return e0 + int64_t(u * 64 + lane) * EPL + q; };
-  auto load = [&](int64_t e0, Reg (&r)[U]) {
+  // indices within the row in 32 bits: V < 2^31, and e0 stays below V + 6 EB
+  const uint32_t Vu = uint32_t(V);
+  auto elem_index = [&](uint32_t e0, int u, int q) -> uint32_t { return e0 + uint32_t((u * 64 + lane) * EPL + q); };
+  auto load = [&](uint32_t e0, Reg (&r)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t e = elem_index(e0, u, 0);
+      const uint32_t e = elem_index(e0, u, 0);
       if constexpr (VEC) {
-        r[u] = e < V ? *reinterpret_cast<const uint4*>(base + e * ESZ) : make_uint4(0, 0, 0, 0);
+        const uint32_t off = e < Vu ? e * uint32_t(ESZ) : 0xFFFFFFF0u;
+        r[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, int(off), 0, 0);
       } else {
-        r[u] = e >= V ? 0u
+        r[u] = e >= Vu ? 0u
                       : (DT == 0 ? reinterpret_cast<const uint32_t*>(base)[e]
                                  : uint32_t(reinterpret_cast<const uint16_t*>(base)[e]));
       }
@@ -181,60 +204,74 @@ void topk_select_kernel(const void* __restrict__ logits, int64_t N, int64_t V, i
   uint64_t thr = 0;  // keys above thr may enter the list
   float thr_f = -INFINITY;
   int n = 0;  // keys in the list (the same in every lane)
-  auto filter = [&](int64_t e0, const Reg (&r)[U]) {
-    if (e0 >= V) return;
-    float m = -INFINITY;
-    if (e0 + EB <= V) {  // a whole batch (uniform): no per-logit bounds test
+  auto filter = [&](uint32_t e0, const Reg (&r)[U]) {
+    if (e0 >= Vu) return;
+    // the max of one load's values (past the row: -inf)
+    auto load_max = [&](int u) -> float {
+      float mx = -INFINITY;
+      if (e0 + EB <= Vu) {  // a whole batch (uniform): no per-logit bounds test
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int q = 0; q < EPL; ++q) mx = fmaxf(mx, value(r, u, q));
+      } else {
 #pragma unroll
-        for (int q = 0; q < EPL; ++q) m = fmaxf(m, value(r, u, q));
-    } else {
+        for (int q = 0; q < EPL; ++q) mx = elem_index(e0, u, q) < Vu ? fmaxf(mx, value(r, u, q)) : mx;
+      }
+      return mx;
+    };
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      // a load none of whose values can enter is skipped whole: one
+      // wave-wide test per load
+      if (__ballot(load_max(u) >= thr_f) != 0) {
+        wave_lds_fence();
 #pragma unroll
         for (int q = 0; q < EPL; ++q) {
           const float x = value(r, u, q);
-          m = elem_index(e0, u, q) < V ? fmaxf(m, x) : m;
+          const uint32_t e = elem_index(e0, u, q);
+          const bool pass = e < Vu && x >= thr_f;
+          if (__ballot(pass) == 0) continue;
+          const uint64_t key = make_key(x, e);
+          const bool take = pass && key > thr;
+          const uint64_t mk = __ballot(take);
+          if (take) cand[n + __popcll(mk & lanes_below(lane))] = key;
+          n += __popcll(mk);
         }
-    }
-    if (__ballot(m >= thr_f) == 0) return;  // nothing in this batch can enter
-    wave_lds_fence();
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) {
-        const float x = value(r, u, q);
-        const int64_t e = elem_index(e0, u, q);
-        const bool pass = e < V && x >= thr_f;
-        if (__ballot(pass) == 0) continue;
-        const uint64_t key = make_key(x, uint32_t(e));
-        const bool take = pass && key > thr;
-        const uint64_t mk = __ballot(take);
-        if (take) cand[n + __popcll(mk & lanes_below(lane))] = key;
-        n += __popcll(mk);
       }
-    wave_lds_fence();
-    if (n >= TRIG && n > K) {
-      thr = cut_list(cand, n, K, lane);
-      thr_f = key_floor(thr);
-      n = K;
+      if ((u + 1) % UH == 0) {
+        // EI logits have entered (n < TRIG before them): cut before the next
+        // EI could overflow the list
+        wave_lds_fence();
+        if (n >= TRIG && n > K) {
+          thr = cut_list(cand, n, K, lane);
+          thr_f = key_floor(thr);
+          n = K;
+        }
+      }
     }
   };
 
   // three register sets: two batches in flight while the third is filtered
   // (a fourth set measured no faster)
+  // The loads go out in the order ra, rb, rc before the loop and in the loop
+  // alike (scheduling barriers keep the compiler from reordering them), so
+  // at the loop head ra's loads are the oldest in both cases and the wait
+  // for them leaves rb's and rc's in flight.
   Reg ra[U], rb[U], rc[U];
-  load(0, ra);
-  load(EB, rb);
-  load(2 * EB, rc);
-  for (int64_t e0 = 0; e0 < V; e0 += 3 * EB) {
+  auto load_in_order = [&](uint32_t e, Reg (&r)[U]) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(e, r);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  load_in_order(0, ra);
+  load_in_order(EB, rb);
+  load_in_order(2 * EB, rc);
+  for (uint32_t e0 = 0; e0 < Vu; e0 += 3 * EB) {
     filter(e0, ra);
-    load(e0 + 3 * EB, ra);
+    load_in_order(e0 + 3 * EB, ra);
     filter(e0 + EB, rb);
-    load(e0 + 4 * EB, rb);
+    load_in_order(e0 + 4 * EB, rb);
     filter(e0 + 2 * EB, rc);
-    load(e0 + 5 * EB, rc);
+    load_in_order(e0 + 5 * EB, rc);
   }
   if (n > K) {
     cut_list(cand, n, K, lane);
@@ -264,6 +301,8 @@ void topk_select_kernel(const void* __restrict__ logits, int64_t N, int64_t V, i
 hipError_t launch_topk_select(const void* logits, int dtype, bool vec, int64_t N, int64_t V, int K,
                               int32_t* idx, float* val, hipStream_t s) {
   const dim3 grid{unsigned((N + TW - 1) / TW), 1, 1}, block{unsigned(TW * 64), 1, 1};
+  // the 16-byte path addresses a row with 32-bit buffer offsets
+  if (V * (dtype == 0 ? 4 : 2) > int64_t(0x7FFFFFF0)) vec = false;
   if (dtype == 0) {
     if (vec)
       hipLaunchKernelGGL((topk_select_kernel<0, true>), grid, block, 0, s, logits, N, V, K, idx, val);
