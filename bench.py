@@ -856,6 +856,12 @@ def main():
     step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
     med = lambda v: v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
     peak_gib = torch.cuda.max_memory_allocated() / 2**30
+    reserved_gib = torch.cuda.max_memory_reserved() / 2**30
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+              "compute_units": props.multi_processor_count,
+              "hbm_gib": round(props.total_memory / 2**30, 1),
+              "peak_basis": "published dense bf16: 256 CUs x 2.4 GHz x 4096 flop/clk/CU"}
     flops_step = 8.0 * cfg.N * cfg.D * cfg.V
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = cfg.N / (ms_per_step * 1e-3)
@@ -908,7 +914,8 @@ def main():
                 "sorted N(0,3) teacher logits)",
         "config": _config_doc(cfg, args.seed),
         "tflops": round(tflops, 1), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "peak_hbm_gib": round(peak_gib, 3),
+        "peak_hbm_gib": round(peak_gib, 3), "peak_reserved_gib": round(reserved_gib, 3),
+        "device": device,
         "median_ms": {"step": round(med(step_ms), 4), "forward": round(med(fwd_ms), 4),
                       "backward": round(med(bwd_ms), 4)},
         "kernel_ms_per_step": {k: round(v["total_ms"] / psteps, 4) for k, v in per_kernel.items()},
