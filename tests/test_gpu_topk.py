@@ -104,6 +104,33 @@ def test_very_long_rows():
     _check(_bf16(r.standard_normal((2, (1 << 21) + 3))), 100, bf16=True)
 
 
+@pytest.mark.parametrize("V,dt", [((0x7FFFFFF0 // 4), "f32"), ((1 << 31) - 1, "f32"), ((1 << 31) - 1, "bf16")])
+def test_rows_at_the_index_limits(V, dt):
+    """One row at the largest sizes: 2^31 - 16 bytes of fp32 (the last row
+    the 16-byte path takes, its offsets at the top of 32 bits) and 2^31 - 1
+    logits (the largest row accepted; the element path, ids up to 2^31 - 2).
+    The row holds -5 everywhere and 8 planted larger values, so the result is
+    known by construction: the planted values best first, then -5 at the
+    lowest free ids."""
+    import torch
+    import lm_head_top_amd as kd
+    K = 16
+    say(f"case topk row at the index limit V={V} {dt}")
+    dtype = torch.float32 if dt == "f32" else torch.bfloat16
+    x = torch.full((1, V), -5.0, dtype=dtype, device="cuda")
+    ids = [V - 1, V - 2, V - 5, V // 2, 123456789, 7, 3, 0]
+    vals = [9.0, 8.5, 8.0, 7.0, 6.5, 6.0, 5.5, 5.0]
+    x[0, torch.tensor(ids, device="cuda")] = torch.tensor(vals, dtype=dtype, device="cuda")
+    idx, val = kd.topk_select(x, K)
+    torch.cuda.synchronize()
+    del x
+    free = [i for i in range(K + len(ids)) if i not in ids][:K - len(ids)]
+    want_i = ids + free
+    want_v = vals + [-5.0] * len(free)
+    assert idx[0].cpu().tolist() == want_i
+    assert val[0].cpu().tolist() == want_v
+
+
 def test_empty_batch():
     import torch
     import lm_head_top_amd as kd
