@@ -10,8 +10,9 @@
 //   teacher   p = softmax_K(t/T) and h = sum p log p per position (one wave per row);
 //   bucket    the chunk's (row, id, k) cache entries, counting-sorted by (position
 //             tile, vocab tile) so each logits tile finds exactly its own entries;
-//   logits    z^T = W H_c^T / T for one 256 x 256 (vocab, position) tile on bf16
-//             MFMA (v_mfma_f32_32x32x16_bf16), then
+//   logits    z^T = W H_c^T / T for 256 x 256 (vocab, position) tiles on bf16
+//             MFMA (v_mfma_f32_32x32x16_bf16), one workgroup per compute unit
+//             walking its tiles in bands of 4 position tiles, then per tile
 //             forward: per-position tile max / sum-exp and the logits at the
 //                      cached ids go to small buffers (never the tile itself);
 //             backward: G = g/(N T) (exp(z - lse) - p scattered at the ids),
