@@ -716,7 +716,8 @@ def main():
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, "
-                         "WRITE_SIZE) of a --copy-calibration-mib run into profiles/traffic.json")
+                         "WRITE_SIZE) of a --copy-calibration-mib run into "
+                         "profiles/traffic_<workload>.json")
     ap.add_argument("--traffic-command", default="",
                     help="with --traffic-from / --stats-from: the profiling command, recorded")
     ap.add_argument("--stats-from", nargs=2, metavar=("STATS_DIR", "OUT_MD"),
