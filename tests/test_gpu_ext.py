@@ -111,6 +111,46 @@ def test_ext_matches_oracle(name):
     _compare(out, ref, name)
 
 
+def _sweep_cases(n=8, seed=20261204):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(r.integers(1, 1200))
+        D = 8 * int(r.integers(1, 65))
+        V = int(r.integers(40, 5001))
+        K = int(r.integers(1, min(V, 256) + 1))
+        chunk = int(r.integers(16, N + 65))
+        T = float(r.choice([0.5, 1.0, 2.0]))
+        alpha, beta = (float(x) for x in r.choice([(1.0, 0.0), (0.5, 0.5), (0.0, 1.0), (0.8, 0.3)]))
+        out.append((i, N, D, V, K, chunk, T, alpha, beta, bool(r.integers(0, 2)),
+                    str(r.choice(["all", "some_missing", "none"])), str(r.choice(["mask", "weights", "none"])),
+                    None if i % 2 else 0.6))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"s{c[0]}")
+def test_ext_sweep(case):
+    """A seeded sweep of shapes and loss settings (weights or a mask or none,
+    labels all, some missing or none, the KL / CE mix, T^2) against the
+    extended oracle."""
+    i, N, D, V, K, chunk, T, alpha, beta, t2, lab, wr, g = case
+    say(f"case ext sweep {i}: N={N} D={D} V={V} K={K} chunk={chunk} T={T} alpha={alpha} beta={beta} "
+        f"T2={t2} labels={lab} weights={wr} grad={g}")
+    cfg = KDConfig("sweep", N=N, D=D, V=V, K=K, chunk=chunk, T=T, ids="uniform", cfg_id=11)
+    inp = make_inputs(cfg, 200 + i)
+    rng = np.random.default_rng(300 + i)
+    y = _labels(None if lab == "none" else lab, N, V, np.asarray(inp["idx"]), rng)
+    w = _weights(None if wr == "none" else wr, N, rng)
+    if w is not None:
+        w = w.astype(np.float32).astype(np.float64)
+        if not w.any():
+            w[0] = 1.0
+    out = _run_ext(inp, T, chunk, labels=y, weights=w, alpha=alpha, beta=beta, scale_T2=t2, grad_loss=g)
+    ref = E.forward_backward_ext(inp["H"], inp["W"], inp["idx"], inp["t"], T, labels=y, weights=w,
+                                 alpha=alpha, beta=beta, scale_T2=t2, grad_loss=1.0 if g is None else g)
+    _compare(out, ref, f"sweep {i}")
+
+
 def test_all_zero_weights_give_zero_loss_and_gradients():
     cfg = KDConfig("zero", N=200, D=64, V=700, K=8, chunk=128, T=1.0, ids="uniform", cfg_id=9)
     say("case ext all-zero weights")
